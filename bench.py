@@ -1,0 +1,214 @@
+#!/usr/bin/env python3
+"""Paged decode attention benchmark on one MI355X.
+
+One step = the whole decode hot path over one batch: the KV write of each
+sequence's new token (reshape_and_cache) followed by decode attention over the
+paged cache (decode kernel + split-K reduce).  Inputs are the seeded synthetic
+workload, resident in HBM before timing starts.
+
+Prints ONE JSON line.  ``value`` is whole-step throughput in GB/s of
+algorithmic bytes (K/V of every context token once -- shared prefix pages once
+-- plus q in, out, the block-table entries used, the lengths, and the KV-write
+rows); ``seqs_per_s`` is sequences decoded per second.  ``roofline`` rates the
+decode kernel alone (its launches timed with HIP events on the library's
+stream) against the MI355X HBM peak; ``cpu_baseline`` is the float64 oracle
+on the host cores over a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+
+
+def parse_args(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="llama7b",
+                    help="workload: tiny, llama7b, gqa, shared_prefix, long_context")
+    ap.add_argument("--partition-size", type=int, default=None,
+                    help="override the workload's partition size (0 = single pass)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle sample")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="time only the decode call per step (profiling aid)")
+    return ap.parse_args(argv)
+
+
+def kernel_source_hash() -> str:
+    """Hash of the decode kernel sources, to tell whether stored counters
+    still describe the code being run."""
+    h = hashlib.sha256()
+    for f in ("common.h", "launch.h", "decode_valu.hip", "decode_mfma.hip", "reduce.hip",
+              "api.cpp"):
+        with open(os.path.join(ROOT, "paged_kv_cache_269_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(config: str):
+    """HBM bytes per decode launch from the committed rocprofv3 counter summary,
+    if it was taken on the current kernel sources and this workload."""
+    path = os.path.join(ROOT, "profiles", f"decode_{config}_counters.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_hash = re.search(r"source-hash:\s*([0-9a-f]+)", text)
+    m_bytes = re.search(r"hbm-bytes-per-launch:\s*([0-9.eE+]+)", text)
+    if not (m_hash and m_bytes) or m_hash.group(1) != kernel_source_hash():
+        return None
+    return float(m_bytes.group(1))
+
+
+def cpu_baseline(w, target_s: float):
+    """The oracle, untuned, on a prefix of the workload's sequences sized to
+    about target_s seconds on all host threads."""
+    import numpy as np
+    import oracle
+    from paged_kv_cache_269_amd import workloads as W
+
+    threads = oracle.max_threads()
+    Hq = w.num_q_heads
+
+    def run(nseq):
+        seqs = np.repeat(np.arange(nseq), Hq)
+        heads = np.tile(np.arange(Hq), nseq)
+        t0 = time.perf_counter()
+        oracle.decode_rows(w.q, w.k_cache, w.v_cache, w.block_tables, w.context_lens, w.scale,
+                           w.dtype, seqs, heads, num_threads=threads)
+        return time.perf_counter() - t0
+
+    t1 = run(1)
+    n = int(min(w.num_seqs, max(1, target_s / max(t1, 1e-6))))
+    dt = run(n) if n > 1 else t1
+    sub_lens = w.context_lens[:n].astype(np.int64)
+    per_tok = W.kv_bytes_per_token(w.num_kv_heads, w.head_dim, w.elem_bytes)
+    if w.shared_prefix_blocks:
+        prefix = 16 * w.shared_prefix_blocks
+        kv = (prefix + int((sub_lens - prefix).sum())) * per_tok
+    else:
+        kv = int(sub_lens.sum()) * per_tok
+    return {"value": round(kv / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "seqs_per_s": round(n / dt, 3), "seconds": round(dt, 3),
+            "sample": f"first {n} of {w.num_seqs} sequences, all {Hq} query heads, "
+                      f"float64 C oracle with OpenMP"}
+
+
+def main(argv=None) -> int:
+    args = parse_args(argv)
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU; "
+                                   f"--gpus {args.gpus} is not supported (no multi-GPU path "
+                                   "in this build)"}))
+        return 2
+
+    import numpy as np
+    import torch
+    import paged_kv_cache_269_amd as pa
+    from paged_kv_cache_269_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        return 1
+    dev = torch.device("cuda:0")
+    pa.load_library()
+
+    w = W.generate(args.config, poison=False)
+    part = w.partition_size if args.partition_size is None else args.partition_size
+    d = W.to_device(w, dev)
+    out = torch.empty_like(d["q"])
+    ws_bytes = pa.decode_workspace_bytes(w.num_seqs, w.num_q_heads, w.head_dim,
+                                         w.max_context_len, part)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def reshape():
+        pa.reshape_and_cache(d["key"], d["value"], d["k_cache"], d["v_cache"],
+                             d["slot_mapping"], stream=stream)
+
+    def decode():
+        pa.paged_attention_decode(out, d["q"], d["k_cache"], d["v_cache"], d["block_tables"],
+                                  d["context_lens"], w.scale, w.max_context_len,
+                                  partition_size=part, workspace=ws, stream=stream)
+
+    for _ in range(args.warmup):
+        if not args.decode_only:
+            reshape()
+        decode()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        if not args.decode_only:
+            reshape()
+        ev[i][0].record(stream)
+        decode()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    dec_ms = np.array([a.elapsed_time(b) for a, b in ev])
+
+    ab = W.algorithmic_bytes(w, unique=True)
+    step_bytes = ab["total"] + (0 if args.decode_only else W.reshape_bytes(w))
+    ms_per_step = wall * 1e3 / K
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    dec_avg = float(dec_ms.mean())
+    achieved = ab["total"] / (dec_avg * 1e-3) / 1e9
+    traffic = stored_traffic(args.config)
+
+    result = {
+        "metric": "paged decode attention: KV GB/s (% of HBM peak) and seqs/s, 7B shape",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) q/K/V, randomly permuted 16-token blocks)",
+        "config": {"workload": w.name, "num_seqs": w.num_seqs, "num_q_heads": w.num_q_heads,
+                   "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "block_size": 16,
+                   "kv_dtype": w.dtype, "accumulate": "f32", "partition_size": part,
+                   "context_len_mean": float(w.context_lens.mean()),
+                   "context_len_max": int(w.max_context_len), "num_blocks": w.num_blocks,
+                   "step": "decode only" if args.decode_only else "reshape_and_cache + decode + reduce"},
+        "seqs_per_s": round(w.num_seqs / (ms_per_step * 1e-3), 1),
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
+        "bytes_per_step": {"algorithmic": step_bytes, "kv_unique": ab["kv"],
+                           "kv_logical": ab["logical_kv"]},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic,
+                     "kernel": "decode (decode kernel + split-K reduce, one library call)",
+                     "launch_us_avg": round(dec_avg * 1e3, 2),
+                     "launch_us_p10": round(float(np.percentile(dec_ms, 10)) * 1e3, 2),
+                     "launch_us_p90": round(float(np.percentile(dec_ms, 90)) * 1e3, 2),
+                     "algorithmic_bytes_per_launch": ab["total"]},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

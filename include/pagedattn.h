@@ -1,0 +1,174 @@
+/*
+ * libpagedattn -- paged KV-cache decode attention for AMD Instinct MI355X
+ * (gfx950).  Plain C ABI: pointers and sizes only.
+ *
+ * Pages defining the operations:
+ *   [CX] "vLLM 2026 推理引擎全解：从 PagedAttention 到分离式 Prefill"
+ *        (chenxutan.com/d/4119.html): §1.1 decode attention
+ *        o_t = Attention(q_t, K_{1:t}, V_{1:t}) over cached K/V; §2.1 the
+ *        cache cut into fixed 16-token pages found through a per-request page
+ *        table, pages anywhere in memory and shareable between requests;
+ *        §2.2 cache layout [num_pages, num_heads, page_size, head_dim] and
+ *        the in-pool token address page_id * BLOCK_SIZE + page_offset.
+ *   [MJ] vLLM tutorial (mjmagnets.cn/news/49643), §2.2: the attention op
+ *        gathers K and V blocks named by the block table, then computes.
+ *   [DM] vLLM project manual (doramagic.ai/projects/vllm/manual), PagedAttention
+ *        V1/V2 kernels: paged KV reads, wavefront-level reductions, fused
+ *        kernel, wide vector loads.
+ *
+ * Common conventions
+ *   - Element types (dtype): PA_F32, PA_F16 (IEEE binary16), PA_BF16.  q,
+ *     key, value, the caches and out share one type; all arithmetic inside
+ *     is float32.
+ *   - Layouts (row-major, contiguous):
+ *       q, out             [num_seqs, num_q_heads, head_dim]
+ *       key, value         [num_tokens, num_kv_heads, head_dim]
+ *       k_cache, v_cache   [num_blocks, num_kv_heads, block_size, head_dim]
+ *       block_tables       [num_seqs, max_blocks_per_seq] int32
+ *       context_lens       [num_seqs] int32
+ *       slot_mapping       [num_tokens] int64
+ *     Logical token t of sequence s lives in block block_tables[s][t / 16]
+ *     at offset t % 16.  context_lens[s] counts every cached token, the one
+ *     being decoded included.  Query head h reads KV head
+ *     h / (num_q_heads / num_kv_heads).
+ *   - Pointers are device pointers on the current HIP device, owned by the
+ *     caller; the library allocates, frees and synchronises nothing.  Every
+ *     call is enqueued on `stream` (a hipStream_t; NULL = the null stream)
+ *     and returns before the work completes.  Calls keep no state.
+ *   - Every argument a host can check is checked before anything is
+ *     launched; a failed check returns its status and launches nothing.
+ *     Device-side contents are not checked for validity, but the kernels
+ *     never read or write outside the buffers the arguments describe:
+ *     block ids outside [0, num_blocks) are skipped, context lengths are
+ *     clamped to [0, min(max_context_len, 16 * max_blocks_per_seq)], and
+ *     slots outside [0, 16 * num_blocks) are not written.
+ *   - No C++ exception crosses this interface.
+ */
+#ifndef PAGEDATTN_H
+#define PAGEDATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum pa_dtype { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 };
+
+enum pa_status {
+  PA_OK = 0,
+  PA_ERR_NULL = 1,        /* a required pointer is NULL */
+  PA_ERR_SHAPE = 2,       /* a size is out of range, or num_q_heads % num_kv_heads != 0 */
+  PA_ERR_UNSUPPORTED = 3, /* head_dim not 64/128, block_size not 16, unknown dtype,
+                             partition_size not a positive multiple of 16 (or 0) */
+  PA_ERR_WORKSPACE = 4,   /* workspace missing or smaller than pa_decode_workspace_bytes */
+  PA_ERR_RANGE = 5,       /* host table check: an entry, length or slot out of range */
+  PA_ERR_LAUNCH = 6       /* the HIP runtime refused a launch */
+};
+
+/*
+ * KV write ([CX] §1.1: the new tokens' K and V are stored in the cache;
+ * [CX] §2.2: token address = block * 16 + offset).  For each token i with
+ * 0 <= slot = slot_mapping[i] < 16 * num_blocks:
+ *     k_cache[slot / 16, h, slot % 16, :] = key[i, h, :]   for every h
+ *     v_cache[slot / 16, h, slot % 16, :] = value[i, h, :]
+ * A bit copy.  Negative slots mean "no write" (padding).  Two tokens with
+ * the same slot leave either one's row in it (a caller error).
+ * block_size must be 16; head_dim 64 or 128.  num_tokens = 0 is a no-op.
+ */
+int pa_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
+                         const int64_t* slot_mapping, int32_t num_tokens,
+                         int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                         int64_t num_blocks, int32_t dtype, void* stream);
+
+/*
+ * Decode attention over the paged cache ([CX] §1.1, §2.1-§2.2; [MJ] §2.2):
+ * for every sequence s and query head h, with L = context_lens[s],
+ * g = h / (num_q_heads / num_kv_heads), b_t = block_tables[s][t / 16]:
+ *     z_t = scale * sum_d q[s,h,d] * k_cache[b_t, g, t % 16, d]
+ *     out[s,h,:] = sum_{t<L} exp(z_t - max z) v_cache[b_t, g, t % 16, :]
+ *                  / sum_{t<L} exp(z_t - max z)
+ * rounded to nearest-even into out's type.  L = 0 gives a zero row.
+ *
+ * partition_size = 0 processes each sequence in one pass.  Otherwise it must
+ * be a multiple of 16: each sequence is cut into ceil(L / partition_size)
+ * partitions, processed in parallel, and sequences with more than one are
+ * merged by the log-sum-exp reduce (pa_paged_attention_reduce), all on
+ * `stream`.  The partials live in `workspace`, which must hold at least
+ * pa_decode_workspace_bytes(num_seqs, num_q_heads, head_dim,
+ * max_context_len, partition_size) bytes (may be NULL when that is 0).
+ * max_context_len is a host-side bound on context_lens (sizes the grid);
+ * longer contexts are clamped to it.  Tail slots of a sequence's last block
+ * and blocks past ceil(L / 16) are never used, whatever they hold.
+ */
+int pa_paged_attention_decode(void* out, const void* q, const void* k_cache,
+                              const void* v_cache, const int32_t* block_tables,
+                              const int32_t* context_lens, int32_t num_seqs,
+                              int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                              int32_t block_size, int32_t max_blocks_per_seq,
+                              int64_t num_blocks, float scale, int32_t dtype,
+                              int32_t partition_size, int32_t max_context_len,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Split-K merge.  Sequence s has P = ceil(L / partition_size) partitions,
+ * L = context_lens[s] clamped to [0, partition_size * max_partitions].  For
+ * query head h the partials are
+ *     max_logits[s,h,p] = max of scale * q.k_t over partition p's tokens
+ *     exp_sums[s,h,p]   = sum of exp(z_t - max_logits[s,h,p]) over them
+ *     tmp_out[s,h,p,:]  = sum exp(z_t - max_logits) v_t / exp_sums   (normalised)
+ * and the result is
+ *     M = max_p max_logits,  w_p = exp_sums * exp(max_logits - M),
+ *     out[s,h,:] = sum_p w_p tmp_out[s,h,p,:] / sum_p w_p
+ * rounded into out's type (P = 1 copies the single partial, P = 0 writes
+ * zeros).  Layouts: max_logits, exp_sums [num_seqs, num_q_heads,
+ * max_partitions] float32; tmp_out [num_seqs, num_q_heads, max_partitions,
+ * head_dim] float32.  Entries p >= P are not read.
+ */
+int pa_paged_attention_reduce(void* out, const float* max_logits, const float* exp_sums,
+                              const float* tmp_out, const int32_t* context_lens,
+                              int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                              int32_t partition_size, int32_t max_partitions, int32_t dtype,
+                              void* stream);
+
+/*
+ * Workspace bytes pa_paged_attention_decode needs for these sizes: 0 for
+ * partition_size = 0 or when every sequence fits one partition, else room
+ * for tmp_out, max_logits and exp_sums with
+ * max_partitions = ceil(max_context_len / partition_size).  Returns 0 for
+ * invalid arguments (which the decode call then rejects).
+ */
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                 int32_t max_context_len, int32_t partition_size);
+
+/*
+ * Host-side check of block tables (host pointers): every entry a sequence
+ * uses, logical blocks 0 .. ceil(L/block_size)-1, must lie in
+ * [0, num_blocks), ceil(L/block_size) must not exceed max_blocks_per_seq and
+ * L must be >= 0.  Returns PA_OK, PA_ERR_RANGE, PA_ERR_NULL or PA_ERR_SHAPE.
+ * Touches no GPU.
+ */
+int pa_validate_tables_host(const int32_t* block_tables, const int32_t* context_lens,
+                            int32_t num_seqs, int32_t max_blocks_per_seq,
+                            int64_t num_blocks, int32_t block_size);
+
+/*
+ * Host-side check of a slot mapping (host pointer): every slot is negative
+ * or below 16 * num_blocks, and no two non-negative slots are equal.
+ * Returns PA_OK, PA_ERR_RANGE, PA_ERR_NULL or PA_ERR_SHAPE.
+ */
+int pa_validate_slots_host(const int64_t* slot_mapping, int32_t num_tokens,
+                           int64_t num_blocks, int32_t block_size);
+
+/* Static description of a status code. */
+const char* pa_status_string(int status);
+
+/* Library version string. */
+const char* pa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDATTN_H */

@@ -1,0 +1,28 @@
+"""paged_kv_cache_269_amd: PagedAttention decode for AMD Instinct MI355X (gfx950).
+
+Thin Python binding over ``libpagedattn.so`` (C ABI in ``include/pagedattn.h``).
+It only marshals torch tensors (device memory) and streams into the library's
+entry points; every step of the computation runs in the library's HIP
+kernels.  Importing the package never loads the library; the first call does,
+and raises if the library is missing -- there is no fallback path.
+"""
+from ._binding import (  # noqa: F401
+    PagedAttnError,
+    decode_workspace_bytes,
+    lib_path,
+    load_library,
+    paged_attention_decode,
+    paged_attention_reduce,
+    reshape_and_cache,
+    status_string,
+    validate_slots_host,
+    validate_tables_host,
+    version,
+    EXPORTS,
+)
+
+__all__ = [
+    "PagedAttnError", "decode_workspace_bytes", "lib_path", "load_library",
+    "paged_attention_decode", "paged_attention_reduce", "reshape_and_cache",
+    "status_string", "validate_slots_host", "validate_tables_host", "version", "EXPORTS",
+]

@@ -1,0 +1,235 @@
+// C-ABI host layer of libpagedattn: argument checks, kernel choice, launches.
+// Declarations and the meaning of every argument: include/pagedattn.h.
+#include "../../include/pagedattn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <climits>
+#include <cstdint>
+#include <vector>
+
+#include "launch.h"
+
+namespace {
+
+constexpr int kBlock = 16;
+constexpr int kMaxGridYZ = 65535;
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int elem_bytes(int32_t dtype) {
+  switch (dtype) {
+    case PA_F32: return 4;
+    case PA_F16: return 2;
+    case PA_BF16: return 2;
+    default: return 0;
+  }
+}
+
+bool head_dim_ok(int32_t d) { return d == 64 || d == 128; }
+
+struct WsLayout {
+  size_t tmp_out = 0, max_logits = 0, exp_sums = 0, total = 0;
+};
+
+// Partials layout for P partitions: [tmp_out | max_logits | exp_sums].
+WsLayout ws_layout(int64_t num_seqs, int64_t heads, int64_t head_dim, int64_t parts) {
+  WsLayout w;
+  if (parts <= 1) return w;
+  const size_t rows = (size_t)num_seqs * heads * parts;
+  w.tmp_out = 0;
+  w.max_logits = align256(rows * head_dim * sizeof(float));
+  w.exp_sums = w.max_logits + align256(rows * sizeof(float));
+  w.total = w.exp_sums + align256(rows * sizeof(float));
+  return w;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_version(void) { return "libpagedattn 0.1.0 (gfx950)"; }
+
+const char* pa_status_string(int status) {
+  switch (status) {
+    case PA_OK: return "ok";
+    case PA_ERR_NULL: return "a required pointer is NULL";
+    case PA_ERR_SHAPE: return "a size is out of range or num_q_heads is not a multiple of num_kv_heads";
+    case PA_ERR_UNSUPPORTED: return "unsupported head_dim, block_size, dtype or partition_size";
+    case PA_ERR_WORKSPACE: return "workspace missing or too small";
+    case PA_ERR_RANGE: return "table entry, context length or slot out of range";
+    case PA_ERR_LAUNCH: return "the HIP runtime refused a kernel launch";
+    default: return "unknown status";
+  }
+}
+
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                 int32_t max_context_len, int32_t partition_size) {
+  if (num_seqs < 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len < 0 ||
+      partition_size < 0)
+    return 0;
+  if (partition_size == 0) return 0;
+  const int64_t parts = ceil_div(max_context_len, partition_size);
+  return ws_layout(num_seqs, num_q_heads, head_dim, parts).total;
+}
+
+int pa_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
+                         const int64_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
+                         int32_t head_dim, int32_t block_size, int64_t num_blocks, int32_t dtype,
+                         void* stream) {
+  const int eb = elem_bytes(dtype);
+  if (!eb || block_size != kBlock || !head_dim_ok(head_dim)) return PA_ERR_UNSUPPORTED;
+  if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks <= 0) return PA_ERR_SHAPE;
+  if (num_tokens == 0) return PA_OK;
+  if (!key || !value || !k_cache || !v_cache || !slot_mapping) return PA_ERR_NULL;
+  hipError_t e = pa::launch_reshape_and_cache(key, value, k_cache, v_cache, slot_mapping,
+                                              num_tokens, num_kv_heads, head_dim, eb, num_blocks,
+                                              (hipStream_t)stream);
+  return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+int pa_paged_attention_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* block_tables, const int32_t* context_lens,
+                              int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                              int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                              int64_t num_blocks, float scale, int32_t dtype,
+                              int32_t partition_size, int32_t max_context_len, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  if (!elem_bytes(dtype) || block_size != kBlock || !head_dim_ok(head_dim))
+    return PA_ERR_UNSUPPORTED;
+  if (partition_size < 0 || partition_size % kBlock) return PA_ERR_UNSUPPORTED;
+  if (num_seqs < 0 || num_seqs > kMaxGridYZ || num_q_heads <= 0 || num_q_heads > kMaxGridYZ ||
+      num_kv_heads <= 0 || num_q_heads % num_kv_heads || max_blocks_per_seq <= 0 ||
+      num_blocks <= 0 || max_context_len < 0)
+    return PA_ERR_SHAPE;
+  if (num_seqs == 0) return PA_OK;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return PA_ERR_NULL;
+
+  // Longest context any kernel will look at.
+  const int64_t max_len = std::min<int64_t>(max_context_len, (int64_t)max_blocks_per_seq * kBlock);
+  const int64_t table_blocks = ceil_div(std::max<int64_t>(max_len, 1), kBlock);
+  int64_t part_blocks, parts;
+  if (partition_size == 0) {
+    part_blocks = table_blocks;
+    parts = 1;
+  } else {
+    part_blocks = partition_size / kBlock;
+    parts = std::max<int64_t>(1, ceil_div(max_len, partition_size));
+  }
+  if (parts > INT_MAX) return PA_ERR_SHAPE;
+
+  const WsLayout ws = ws_layout(num_seqs, num_q_heads, head_dim, parts);
+  if (ws.total && (!workspace || workspace_bytes < ws.total)) return PA_ERR_WORKSPACE;
+
+  pa::DecodeArgs a{};
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  char* wsb = static_cast<char*>(workspace);
+  a.tmp_out = ws.total ? reinterpret_cast<float*>(wsb + ws.tmp_out) : nullptr;
+  a.max_logits = ws.total ? reinterpret_cast<float*>(wsb + ws.max_logits) : nullptr;
+  a.exp_sums = ws.total ? reinterpret_cast<float*>(wsb + ws.exp_sums) : nullptr;
+  a.num_blocks_i32 = (int)std::min<int64_t>(num_blocks, INT32_MAX);
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.max_len = (int)max_len;
+  a.part_blocks = (int)part_blocks;
+  a.max_partitions = (int)parts;
+  a.scale_log2 = scale * 1.4426950408889634f;
+
+  const hipStream_t st = (hipStream_t)stream;
+  const int group = num_q_heads / num_kv_heads;
+  // Grouped heads share every K/V tile: a matrix-core product pays off from
+  // two heads up.  Single heads and fp32 stay on the vector ALU.
+  const bool use_mfma = dtype != PA_F32 && group >= 2;
+  hipError_t e = use_mfma ? pa::launch_decode_mfma(a, dtype, head_dim, num_seqs, st)
+                          : pa::launch_decode_valu(a, dtype, head_dim, num_seqs, st);
+  if (e != hipSuccess) return PA_ERR_LAUNCH;
+  if (parts > 1) {
+    pa::ReduceArgs r{};
+    r.out = out;
+    r.max_logits = a.max_logits;
+    r.exp_sums = a.exp_sums;
+    r.tmp_out = a.tmp_out;
+    r.context_lens = context_lens;
+    r.num_q_heads = num_q_heads;
+    r.partition_size = partition_size;
+    r.max_partitions = (int)parts;
+    r.max_len = (int)max_len;
+    r.skip_single = 1;
+    e = pa::launch_reduce(r, dtype, head_dim, num_seqs, st);
+    if (e != hipSuccess) return PA_ERR_LAUNCH;
+  }
+  return PA_OK;
+}
+
+int pa_paged_attention_reduce(void* out, const float* max_logits, const float* exp_sums,
+                              const float* tmp_out, const int32_t* context_lens, int32_t num_seqs,
+                              int32_t num_q_heads, int32_t head_dim, int32_t partition_size,
+                              int32_t max_partitions, int32_t dtype, void* stream) {
+  if (!elem_bytes(dtype) || !head_dim_ok(head_dim)) return PA_ERR_UNSUPPORTED;
+  if (partition_size <= 0) return PA_ERR_UNSUPPORTED;
+  if (num_seqs < 0 || num_seqs > kMaxGridYZ || num_q_heads <= 0 || max_partitions <= 0)
+    return PA_ERR_SHAPE;
+  if (num_seqs == 0) return PA_OK;
+  if (!out || !max_logits || !exp_sums || !tmp_out || !context_lens) return PA_ERR_NULL;
+  pa::ReduceArgs r{};
+  r.out = out;
+  r.max_logits = max_logits;
+  r.exp_sums = exp_sums;
+  r.tmp_out = tmp_out;
+  r.context_lens = context_lens;
+  r.num_q_heads = num_q_heads;
+  r.partition_size = partition_size;
+  r.max_partitions = max_partitions;
+  r.max_len = (int)std::min<int64_t>((int64_t)partition_size * max_partitions, INT_MAX);
+  r.skip_single = 0;
+  hipError_t e = pa::launch_reduce(r, dtype, head_dim, num_seqs, (hipStream_t)stream);
+  return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+int pa_validate_tables_host(const int32_t* block_tables, const int32_t* context_lens,
+                            int32_t num_seqs, int32_t max_blocks_per_seq, int64_t num_blocks,
+                            int32_t block_size) {
+  if (num_seqs < 0 || max_blocks_per_seq <= 0 || num_blocks < 0 || block_size <= 0)
+    return PA_ERR_SHAPE;
+  if (num_seqs == 0) return PA_OK;
+  if (!block_tables || !context_lens) return PA_ERR_NULL;
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    const int32_t L = context_lens[s];
+    if (L < 0) return PA_ERR_RANGE;
+    const int64_t used = ceil_div(L, block_size);
+    if (used > max_blocks_per_seq) return PA_ERR_RANGE;
+    const int32_t* row = block_tables + (int64_t)s * max_blocks_per_seq;
+    for (int64_t j = 0; j < used; ++j)
+      if (row[j] < 0 || row[j] >= num_blocks) return PA_ERR_RANGE;
+  }
+  return PA_OK;
+}
+
+int pa_validate_slots_host(const int64_t* slot_mapping, int32_t num_tokens, int64_t num_blocks,
+                           int32_t block_size) {
+  if (num_tokens < 0 || num_blocks < 0 || block_size <= 0) return PA_ERR_SHAPE;
+  if (num_tokens == 0) return PA_OK;
+  if (!slot_mapping) return PA_ERR_NULL;
+  const int64_t limit = num_blocks * block_size;
+  std::vector<int64_t> used;
+  used.reserve(num_tokens);
+  for (int32_t i = 0; i < num_tokens; ++i) {
+    const int64_t slot = slot_mapping[i];
+    if (slot >= limit) return PA_ERR_RANGE;
+    if (slot >= 0) used.push_back(slot);
+  }
+  std::sort(used.begin(), used.end());
+  if (std::adjacent_find(used.begin(), used.end()) != used.end()) return PA_ERR_RANGE;
+  return PA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,174 @@
+// Device-side helpers shared by the gfx950 kernels of libpagedattn:
+// element-type traits, 16-byte vector access, wave64 cross-lane reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+enum Dtype : int { kF32 = 0, kF16 = 1, kBF16 = 2 };
+
+constexpr int kBlockSize = 16;   // tokens per physical block
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+template <int DT> struct Elem;
+template <> struct Elem<kF32> { static constexpr int bytes = 4; };
+template <> struct Elem<kF16> { static constexpr int bytes = 2; };
+template <> struct Elem<kBF16> { static constexpr int bytes = 2; };
+
+// ---------------------------------------------------------------------------
+// element <-> float
+//
+// Reinterpreting casts go through these by-value helpers: with this hipcc,
+// __builtin_bit_cast applied directly to an ext_vector element (v[k], v.z)
+// reads element 0 instead of element k, so a vector element is always first
+// copied into a scalar.
+
+__device__ __forceinline__ float u2f(uint32_t u) { return __builtin_bit_cast(float, u); }
+__device__ __forceinline__ uint32_t f2u(float f) { return __builtin_bit_cast(uint32_t, f); }
+__device__ __forceinline__ f16x2 u2h2(uint32_t u) { return __builtin_bit_cast(f16x2, u); }
+__device__ __forceinline__ bf16x2 u2b2(uint32_t u) { return __builtin_bit_cast(bf16x2, u); }
+
+// The two 16-bit elements of a 32-bit word, as floats (low half first).
+template <int DT>
+__device__ __forceinline__ void unpack2(uint32_t w, float& lo, float& hi) {
+  if constexpr (DT == kF16) {
+    const f16x2 h = u2h2(w);
+    lo = (float)h.x;
+    hi = (float)h.y;
+  } else {
+    lo = u2f(w << 16);
+    hi = u2f(w & 0xffff0000u);
+  }
+}
+
+// float -> 16-bit storage, round to nearest even.
+template <int DT>
+__device__ __forceinline__ uint16_t to_bits16(float x) {
+  if constexpr (DT == kF16) {
+    return __builtin_bit_cast(uint16_t, (_Float16)x);
+  } else {
+    return __builtin_bit_cast(uint16_t, (__bf16)x);
+  }
+}
+
+// Store one float result into an element array of type DT.
+template <int DT>
+__device__ __forceinline__ void store_elem(void* base, int64_t idx, float x) {
+  if constexpr (DT == kF32) {
+    reinterpret_cast<float*>(base)[idx] = x;
+  } else {
+    reinterpret_cast<uint16_t*>(base)[idx] = to_bits16<DT>(x);
+  }
+}
+
+// Dot product of two 16-byte chunks (4 f32 or 8 f16/bf16 elements), fp32
+// accumulation onto acc.
+template <int DT>
+__device__ __forceinline__ float dot16(const u32x4& a, const u32x4& b, float acc) {
+  if constexpr (DT == kF32) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      acc = __builtin_fmaf(u2f(a[k]), u2f(b[k]), acc);
+  } else if constexpr (DT == kF16) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      acc = __builtin_amdgcn_fdot2(u2h2(a[k]), u2h2(b[k]), acc, false);
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      acc = __builtin_amdgcn_fdot2_f32_bf16(u2b2(a[k]), u2b2(b[k]), acc, false);
+  }
+  return acc;
+}
+
+// acc[0..VEC) += p * chunk, VEC = 16 / element bytes.
+template <int DT>
+__device__ __forceinline__ void axpy16(float p, const u32x4& v, float* acc) {
+  if constexpr (DT == kF32) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) acc[k] = __builtin_fmaf(p, u2f(v[k]), acc[k]);
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      float lo, hi;
+      unpack2<DT>(v[k], lo, hi);
+      acc[2 * k] = __builtin_fmaf(p, lo, acc[2 * k]);
+      acc[2 * k + 1] = __builtin_fmaf(p, hi, acc[2 * k + 1]);
+    }
+  }
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---------------------------------------------------------------------------
+// wave64 cross-lane reductions
+
+// DPP row controls (a DPP row is 16 lanes).
+constexpr int kDppQuadXor1 = 0xB1;   // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;   // quad_perm [2,3,0,1]
+constexpr int kDppRowMirror = 0x140; // lane i <-> 15 - i within a row
+constexpr int kDppHalfMirror = 0x141;// lane i <-> 7 - i within each half row
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return u2f((uint32_t)__builtin_amdgcn_update_dpp(0, (int)f2u(x), CTRL, 0xF, 0xF, false));
+}
+
+// Exchange with lane ^ 16 / lane ^ 32, combined through op.  The gfx950
+// permlane swaps hand back both halves of the exchange; combining the two
+// results lane-wise gives op(x[l], x[l ^ 16]) (resp. ^ 32) in every lane.
+template <typename Op>
+__device__ __forceinline__ float xor16_combine(float x, Op op) {
+  auto r = __builtin_amdgcn_permlane16_swap(f2u(x), f2u(x), false, false);
+  const uint32_t a = r[0], b = r[1];
+  return op(u2f(a), u2f(b));
+}
+template <typename Op>
+__device__ __forceinline__ float xor32_combine(float x, Op op) {
+  auto r = __builtin_amdgcn_permlane32_swap(f2u(x), f2u(x), false, false);
+  const uint32_t a = r[0], b = r[1];
+  return op(u2f(a), u2f(b));
+}
+
+struct AddOp {
+  __device__ __forceinline__ float operator()(float a, float b) const { return a + b; }
+};
+struct MaxOp {
+  __device__ __forceinline__ float operator()(float a, float b) const { return __builtin_fmaxf(a, b); }
+};
+
+// Reduction over aligned groups of N lanes (N in {2,4,8,16,32,64}); every
+// lane of a group receives the group's result.  Within a 16-lane row the
+// butterfly is xor 1, xor 2, then the half-row and row mirrors (each pairs
+// every lane with one from the other half of its current group).
+template <int N, typename Op>
+__device__ __forceinline__ float group_reduce(float x, Op op) {
+  static_assert(N == 2 || N == 4 || N == 8 || N == 16 || N == 32 || N == 64, "group size");
+  x = op(x, dpp<kDppQuadXor1>(x));
+  if constexpr (N >= 4) x = op(x, dpp<kDppQuadXor2>(x));
+  if constexpr (N >= 8) x = op(x, dpp<kDppHalfMirror>(x));
+  if constexpr (N >= 16) x = op(x, dpp<kDppRowMirror>(x));
+  if constexpr (N >= 32) x = xor16_combine(x, op);
+  if constexpr (N >= 64) x = xor32_combine(x, op);
+  return x;
+}
+
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  return group_reduce<N>(x, AddOp{});
+}
+
+}  // namespace pa

@@ -1,0 +1,60 @@
+// Internal launch interface between the C-ABI host layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+// Everything a decode kernel needs, passed by value as one kernel argument.
+struct DecodeArgs {
+  void* out;                    // [B, Hq, D] element type
+  const void* q;                // [B, Hq, D]
+  const void* k_cache;          // [N, Hkv, 16, D]
+  const void* v_cache;          // [N, Hkv, 16, D]
+  const int32_t* block_tables;  // [B, M]
+  const int32_t* context_lens;  // [B]
+  float* tmp_out;               // [B, Hq, P, D] partial outputs (normalised)
+  float* max_logits;            // [B, Hq, P]  (natural-log units)
+  float* exp_sums;              // [B, Hq, P]
+  int num_blocks_i32;           // N, clamped to INT32_MAX (block ids are int32)
+  int num_q_heads;              // Hq
+  int num_kv_heads;             // Hkv
+  int max_blocks_per_seq;       // M
+  int max_len;                  // contexts are clamped to [0, max_len]
+  int part_blocks;              // blocks per partition
+  int max_partitions;           // P (grid x)
+  float scale_log2;             // scale * log2(e)
+};
+
+struct ReduceArgs {
+  void* out;
+  const float* max_logits;
+  const float* exp_sums;
+  const float* tmp_out;
+  const int32_t* context_lens;
+  int num_q_heads;
+  int partition_size;
+  int max_partitions;
+  int max_len;
+  int skip_single;              // 1: sequences with <= 1 partition are left alone
+};
+
+hipError_t launch_reshape_and_cache(const void* key, const void* value, void* k_cache,
+                                    void* v_cache, const int64_t* slot_mapping, int num_tokens,
+                                    int num_kv_heads, int head_dim, int elem_bytes,
+                                    int64_t num_blocks, hipStream_t stream);
+
+// Vector-ALU decode: one workgroup per (partition, query head, sequence).
+hipError_t launch_decode_valu(const DecodeArgs& a, int dtype, int head_dim, int num_seqs,
+                              hipStream_t stream);
+
+// Matrix-core decode for grouped heads: one workgroup per (partition,
+// kv head x 16-head chunk, sequence).
+hipError_t launch_decode_mfma(const DecodeArgs& a, int dtype, int head_dim, int num_seqs,
+                              hipStream_t stream);
+
+hipError_t launch_reduce(const ReduceArgs& a, int dtype, int head_dim, int num_seqs,
+                         hipStream_t stream);
+
+}  // namespace pa

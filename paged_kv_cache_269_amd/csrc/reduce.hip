@@ -1,0 +1,115 @@
+// Split-K merge of partition partials (log-sum-exp reduce).
+//
+// Each partition p of a (sequence, query head) row leaves its score max m_p,
+// its sum l_p = sum exp(z - m_p) and its normalised output o_p.  Because
+// exp(z - M) = exp(z - m_p) exp(m_p - M), softmax over the whole context is
+//   out = sum_p w_p o_p / sum_p w_p,   w_p = l_p exp(m_p - M),  M = max_p m_p.
+// This is the merge the long-context path needs once a context is cut into
+// partitions processed in parallel; it runs after the decode kernel on the
+// same stream.
+//
+// One workgroup (256 lanes) per (query head, sequence): the weights of up to
+// 256 partitions at a time go to LDS, then 256 / head_dim lane groups each
+// sweep a share of those partitions over all head_dim columns (coalesced
+// reads of tmp_out rows), and the shares are added at the end.
+#include "common.h"
+#include "launch.h"
+
+namespace pa {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ float block_max(float x, float* scratch) {
+  x = group_reduce<64>(x, MaxOp{});
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) scratch[w] = x;
+  __syncthreads();
+  float r = scratch[0];
+#pragma unroll
+  for (int i = 1; i < kThreads / 64; ++i) r = __builtin_fmaxf(r, scratch[i]);
+  __syncthreads();
+  return r;
+}
+
+template <int DT, int D>
+__global__ __launch_bounds__(kThreads) void reduce_kernel(ReduceArgs a) {
+  constexpr int SPLIT = kThreads / D;
+  const int h = blockIdx.x, s = blockIdx.y;
+  const int tid = threadIdx.x;
+  int L = a.context_lens[s];
+  L = L < 0 ? 0 : (L > a.max_len ? a.max_len : L);
+  const int P = (L + a.partition_size - 1) / a.partition_size;
+  if (a.skip_single && P <= 1) return;
+  const int64_t orow = (int64_t)s * a.num_q_heads + h;
+  const int64_t base = orow * a.max_partitions;
+
+  __shared__ float s_w[kThreads];
+  __shared__ float s_red[kThreads / 64];
+  __shared__ float s_o[SPLIT][D];
+  __shared__ float s_ws[SPLIT];
+
+  float mx = -INFINITY;
+  for (int p = tid; p < P; p += kThreads) {
+    const float l = a.exp_sums[base + p];
+    if (l > 0.f) mx = __builtin_fmaxf(mx, a.max_logits[base + p]);
+  }
+  const float M = block_max(mx, s_red);
+
+  const int d = tid % D, share = tid / D;
+  float o = 0.f, wsum = 0.f;
+  for (int p0 = 0; p0 < P; p0 += kThreads) {
+    const int p = p0 + tid;
+    float wv = 0.f;
+    if (p < P) {
+      const float l = a.exp_sums[base + p];
+      if (l > 0.f) wv = l * fast_exp2((a.max_logits[base + p] - M) * kLog2e);
+    }
+    s_w[tid] = wv;
+    __syncthreads();
+    const int cnt = min(kThreads, P - p0);
+    for (int k = share; k < cnt; k += SPLIT) {
+      const float ww = s_w[k];
+      wsum += ww;
+      if (ww != 0.f) o += ww * a.tmp_out[(base + p0 + k) * D + d];
+    }
+    __syncthreads();
+  }
+  s_o[share][d] = o;
+  if (d == 0) s_ws[share] = wsum;
+  __syncthreads();
+  if (tid < D) {
+    float ot = 0.f, wt = 0.f;
+#pragma unroll
+    for (int i = 0; i < SPLIT; ++i) {
+      ot += s_o[i][tid];
+      wt += s_ws[i];
+    }
+    store_elem<DT>(a.out, orow * D + tid, wt > 0.f ? ot / wt : 0.f);
+  }
+}
+
+template <int DT, int D>
+hipError_t launch_typed(const ReduceArgs& a, int num_seqs, hipStream_t stream) {
+  hipLaunchKernelGGL((reduce_kernel<DT, D>), dim3(a.num_q_heads, num_seqs), dim3(kThreads), 0,
+                     stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_reduce(const ReduceArgs& a, int dtype, int head_dim, int num_seqs,
+                         hipStream_t stream) {
+  switch (dtype * 1000 + head_dim) {
+    case kF32 * 1000 + 64: return launch_typed<kF32, 64>(a, num_seqs, stream);
+    case kF32 * 1000 + 128: return launch_typed<kF32, 128>(a, num_seqs, stream);
+    case kF16 * 1000 + 64: return launch_typed<kF16, 64>(a, num_seqs, stream);
+    case kF16 * 1000 + 128: return launch_typed<kF16, 128>(a, num_seqs, stream);
+    case kBF16 * 1000 + 64: return launch_typed<kBF16, 64>(a, num_seqs, stream);
+    case kBF16 * 1000 + 128: return launch_typed<kBF16, 128>(a, num_seqs, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace pa

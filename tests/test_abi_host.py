@@ -1,0 +1,141 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments before launching anything."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pagedattn.h")
+
+OK, NULL, SHAPE, UNSUP, WS, RANGE = 0, 1, 2, 3, 4, 5
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation first
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol(hiplib):
+    lib = hiplib.load_library()
+    names = declared_symbols()
+    assert names, "no declarations found"
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(hiplib.EXPORTS) == names
+
+
+def test_version_and_status_strings(hiplib):
+    assert "gfx950" in hiplib.version()
+    for code in range(0, 7):
+        assert hiplib.status_string(code) and hiplib.status_string(code) != "unknown status"
+    assert hiplib.status_string(99) == "unknown status"
+
+
+def _decode(lib, **kw):
+    a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, cl=FAKE, B=2, Hq=8, Hkv=2, D=128, bs=16,
+             M=4, N=10, scale=0.1, dtype=1, part=512, maxlen=64, ws=None, wsb=0, stream=None)
+    a.update(kw)
+    return lib.pa_paged_attention_decode(a["out"], a["q"], a["k"], a["v"], a["bt"], a["cl"],
+                                         a["B"], a["Hq"], a["Hkv"], a["D"], a["bs"], a["M"],
+                                         a["N"], a["scale"], a["dtype"], a["part"], a["maxlen"],
+                                         a["ws"], a["wsb"], a["stream"])
+
+
+def test_decode_argument_checks(hiplib):
+    lib = hiplib.load_library()
+    assert _decode(lib, out=None) == NULL
+    assert _decode(lib, bt=None) == NULL
+    assert _decode(lib, D=96) == UNSUP
+    assert _decode(lib, bs=32) == UNSUP
+    assert _decode(lib, dtype=7) == UNSUP
+    assert _decode(lib, part=100) == UNSUP
+    assert _decode(lib, part=-16) == UNSUP
+    assert _decode(lib, Hq=6, Hkv=4) == SHAPE
+    assert _decode(lib, Hkv=0) == SHAPE
+    assert _decode(lib, B=-1) == SHAPE
+    assert _decode(lib, B=70000) == SHAPE
+    assert _decode(lib, maxlen=-1) == SHAPE
+    assert _decode(lib, N=0) == SHAPE
+    # 1024 tokens in 512-token partitions need partials space
+    assert _decode(lib, maxlen=1024, M=64) == WS
+    need = lib.pa_decode_workspace_bytes(2, 8, 128, 1024, 512)
+    assert _decode(lib, maxlen=1024, M=64, ws=FAKE, wsb=need - 1) == WS
+    # zero sequences: nothing to do, no pointer is looked at
+    assert _decode(lib, B=0, out=None) == OK
+
+
+def test_workspace_bytes(hiplib):
+    lib = hiplib.load_library()
+    f = lib.pa_decode_workspace_bytes
+    assert f(4, 8, 128, 512, 512) == 0          # one partition: no partials
+    assert f(4, 8, 128, 4096, 0) == 0           # single pass
+    rows = 4 * 8 * 2
+    exp = -(-rows * 128 * 4 // 256) * 256 + 2 * (-(-rows * 4 // 256) * 256)
+    assert f(4, 8, 128, 513, 512) == exp
+    assert f(-1, 8, 128, 513, 512) == 0
+
+
+def test_reshape_and_reduce_argument_checks(hiplib):
+    lib = hiplib.load_library()
+    r = lib.pa_reshape_and_cache
+    assert r(None, FAKE, FAKE, FAKE, FAKE, 3, 2, 128, 16, 10, 2, None) == NULL
+    assert r(FAKE, FAKE, FAKE, FAKE, FAKE, 3, 2, 80, 16, 10, 2, None) == UNSUP
+    assert r(FAKE, FAKE, FAKE, FAKE, FAKE, 3, 2, 128, 8, 10, 2, None) == UNSUP
+    assert r(FAKE, FAKE, FAKE, FAKE, FAKE, -3, 2, 128, 16, 10, 2, None) == SHAPE
+    assert r(None, None, None, None, None, 0, 2, 128, 16, 10, 2, None) == OK
+    d = lib.pa_paged_attention_reduce
+    assert d(None, FAKE, FAKE, FAKE, FAKE, 2, 4, 128, 512, 3, 2, None) == NULL
+    assert d(FAKE, FAKE, FAKE, FAKE, FAKE, 2, 4, 128, 0, 3, 2, None) == UNSUP
+    assert d(FAKE, FAKE, FAKE, FAKE, FAKE, 2, 4, 100, 512, 3, 2, None) == UNSUP
+    assert d(FAKE, FAKE, FAKE, FAKE, FAKE, 2, 0, 128, 512, 3, 2, None) == SHAPE
+
+
+@pytest.mark.parametrize("case", range(6))
+def test_table_validator_agrees_with_oracle(hiplib, case):
+    rng = np.random.default_rng(case)
+    B, M, N = 5, 6, 20
+    bt = rng.integers(0, N, size=(B, M)).astype(np.int32)
+    cl = rng.integers(0, M * 16 + 1, size=B).astype(np.int32)
+    if case == 1:
+        bt[2, 0] = N            # used entry out of the pool
+        cl[2] = max(cl[2], 1)
+    if case == 2:
+        cl[0] = M * 16 + 1      # does not fit the row
+    if case == 3:
+        cl[4] = -5
+    if case == 4:
+        bt[1, M - 1] = -7       # only bad if used
+        cl[1] = (M - 1) * 16
+    if case == 5:
+        bt[3, :] = -1           # unused row of an empty sequence
+        cl[3] = 0
+    got = hiplib.validate_tables_host(bt, cl, N)
+    try:
+        oracle.check_tables(bt, cl, N)
+        want = OK
+    except oracle.OracleError:
+        want = RANGE
+    assert got == want
+    assert got == (RANGE if case in (1, 2, 3) else OK)
+
+
+def test_slot_validator(hiplib):
+    assert hiplib.validate_slots_host(np.array([0, 17, -1, -1, 159]), 10) == OK
+    assert hiplib.validate_slots_host(np.array([0, 17, 17]), 10) == RANGE
+    assert hiplib.validate_slots_host(np.array([160]), 10) == RANGE
+    assert hiplib.validate_slots_host(np.zeros(0, np.int64), 10) == OK
+
+
+def test_binding_refuses_host_tensors(hiplib):
+    import torch
+    x = torch.zeros(2, 4, 128, dtype=torch.float16)
+    kc = torch.zeros(3, 4, 16, 128, dtype=torch.float16)
+    with pytest.raises(ValueError):
+        hiplib.reshape_and_cache(x, x, kc, kc, torch.zeros(2, dtype=torch.int64))
