@@ -59,7 +59,9 @@ enum pa_dtype { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 };
 enum pa_status {
   PA_OK = 0,
   PA_ERR_NULL = 1,        /* a required pointer is NULL */
-  PA_ERR_SHAPE = 2,       /* a size is out of range, or num_q_heads % num_kv_heads != 0 */
+  PA_ERR_SHAPE = 2,       /* a size is out of range (num_seqs, num_q_heads and the
+                             partition count are limited to 65535), or
+                             num_q_heads % num_kv_heads != 0 */
   PA_ERR_UNSUPPORTED = 3, /* head_dim not 64/128, block_size not 16, unknown dtype,
                              partition_size not a positive multiple of 16 (or 0) */
   PA_ERR_WORKSPACE = 4,   /* workspace missing or smaller than pa_decode_workspace_bytes */
@@ -95,9 +97,12 @@ int pa_reshape_and_cache(const void* key, const void* value, void* k_cache, void
  * be a multiple of 16: each sequence is cut into ceil(L / partition_size)
  * partitions, processed in parallel, and sequences with more than one are
  * merged by the log-sum-exp reduce (pa_paged_attention_reduce), all on
- * `stream`.  The partials live in `workspace`, which must hold at least
- * pa_decode_workspace_bytes(num_seqs, num_q_heads, head_dim,
- * max_context_len, partition_size) bytes (may be NULL when that is 0).
+ * `stream`.
+ *
+ * The partials live in `workspace` (device memory, caller-owned), which must
+ * hold at least pa_decode_workspace_bytes(num_seqs, num_q_heads, head_dim,
+ * max_context_len, partition_size) bytes (may be NULL when that is 0).  Calls
+ * that share a workspace must not run concurrently.
  * max_context_len is a host-side bound on context_lens (sizes the grid);
  * longer contexts are clamped to it.  Tail slots of a sequence's last block
  * and blocks past ceil(L / 16) are never used, whatever they hold.

@@ -8,6 +8,7 @@ and raises if the library is missing -- there is no fallback path.
 """
 from ._binding import (  # noqa: F401
     PagedAttnError,
+    decode_workspace,
     decode_workspace_bytes,
     lib_path,
     load_library,
@@ -22,7 +23,8 @@ from ._binding import (  # noqa: F401
 )
 
 __all__ = [
-    "PagedAttnError", "decode_workspace_bytes", "lib_path", "load_library",
+    "PagedAttnError", "decode_workspace", "decode_workspace_bytes", "lib_path",
+    "load_library",
     "paged_attention_decode", "paged_attention_reduce", "reshape_and_cache",
     "status_string", "validate_slots_host", "validate_tables_host", "version", "EXPORTS",
 ]

@@ -13,7 +13,9 @@ import os
 from typing import Optional
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "libpagedattn.so")
+# The in-tree build; PAGEDATTN_LIB may name another build of the same sources
+# (tuning variants).
+_LIB_PATH = os.environ.get("PAGEDATTN_LIB") or os.path.join(_HERE, "libpagedattn.so")
 
 PA_OK, PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_UNSUPPORTED = 0, 1, 2, 3
 PA_ERR_WORKSPACE, PA_ERR_RANGE, PA_ERR_LAUNCH = 4, 5, 6
@@ -130,12 +132,21 @@ def decode_workspace_bytes(num_seqs: int, num_q_heads: int, head_dim: int,
                                                         max_context_len, partition_size))
 
 
+def decode_workspace(num_seqs: int, num_q_heads: int, head_dim: int, max_context_len: int,
+                     partition_size: int, device="cuda"):
+    """A uint8 workspace tensor for these sizes (None when none is needed)."""
+    import torch
+    n = decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len, partition_size)
+    return torch.empty(n, dtype=torch.uint8, device=device) if n else None
+
+
 def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale: float,
                            max_context_len: int, partition_size: int = 512, workspace=None,
                            stream=None) -> None:
     """Decode attention into ``out`` [B, Hq, D].  ``workspace`` is a uint8
-    device tensor of at least decode_workspace_bytes(...) bytes (allocated
-    here when omitted -- pass one to keep the call allocation-free)."""
+    device tensor of at least decode_workspace_bytes(...) bytes (see
+    decode_workspace); one is allocated here when needed and omitted -- pass
+    one to keep the call allocation-free."""
     import torch
     B, Hq, D = q.shape
     N, Hkv, bs, D2 = k_cache.shape
@@ -145,9 +156,8 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
         raise TypeError("q, out and caches must share one element type")
     if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.shape != (B,):
         raise ValueError("block_tables must be [num_seqs, max_blocks], context_lens [num_seqs]")
-    need = decode_workspace_bytes(B, Hq, D, max_context_len, partition_size)
-    if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if workspace is None:
+        workspace = decode_workspace(B, Hq, D, max_context_len, partition_size, q.device)
     ws_ptr = _dev_ptr(workspace, "workspace") if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     rc = load_library().pa_paged_attention_decode(

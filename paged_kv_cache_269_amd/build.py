@@ -22,8 +22,8 @@ COMMON_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
                 "-Wall", "-I", os.path.join(ROOT, "include")]
 
 
-def _compile(src: str, extra) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
+def _compile(src: str, extra, build_dir: str) -> str:
+    obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
     cmd = [HIPCC, *COMMON_FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -31,18 +31,21 @@ def _compile(src: str, extra) -> str:
     return obj
 
 
-def build(extra_flags=(), jobs: int = 8) -> str:
-    """Compile every kernel source and link libpagedattn.so; returns its path."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
+def build(extra_flags=(), jobs: int = 8, lib_path: str = LIB_PATH) -> str:
+    """Compile every kernel source and link the library (libpagedattn.so in
+    the package by default); returns its path.  ``extra_flags`` reach every
+    hipcc compile (e.g. -D tuning macros of the kernels)."""
+    build_dir = BUILD_DIR if lib_path == LIB_PATH else lib_path + ".objs"
+    os.makedirs(build_dir, exist_ok=True)
     with ThreadPoolExecutor(min(jobs, len(SOURCES))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, list(extra_flags)), SOURCES))
-    tmp = LIB_PATH + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, list(extra_flags), build_dir), SOURCES))
+    tmp = lib_path + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, lib_path)
+    return lib_path
 
 
 if __name__ == "__main__":

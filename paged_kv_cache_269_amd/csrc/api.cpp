@@ -13,6 +13,10 @@
 
 namespace {
 
+#ifndef PA_MFMA_MIN_GROUP
+#define PA_MFMA_MIN_GROUP 2  // smallest head group sent to the matrix-core kernel
+#endif
+
 constexpr int kBlock = 16;
 constexpr int kMaxGridYZ = 65535;
 
@@ -33,13 +37,13 @@ struct WsLayout {
   size_t tmp_out = 0, max_logits = 0, exp_sums = 0, total = 0;
 };
 
-// Partials layout for P partitions: [tmp_out | max_logits | exp_sums].
+// Partials layout for P > 1 partitions: [tmp_out | max_logits | exp_sums].
 WsLayout ws_layout(int64_t num_seqs, int64_t heads, int64_t head_dim, int64_t parts) {
   WsLayout w;
   if (parts <= 1) return w;
   const size_t rows = (size_t)num_seqs * heads * parts;
   w.tmp_out = 0;
-  w.max_logits = align256(rows * head_dim * sizeof(float));
+  w.max_logits = w.tmp_out + align256(rows * head_dim * sizeof(float));
   w.exp_sums = w.max_logits + align256(rows * sizeof(float));
   w.total = w.exp_sums + align256(rows * sizeof(float));
   return w;
@@ -71,8 +75,7 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
   if (num_seqs < 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len < 0 ||
       partition_size < 0)
     return 0;
-  if (partition_size == 0) return 0;
-  const int64_t parts = ceil_div(max_context_len, partition_size);
+  const int64_t parts = partition_size ? ceil_div(max_context_len, partition_size) : 1;
   return ws_layout(num_seqs, num_q_heads, head_dim, parts).total;
 }
 
@@ -119,7 +122,7 @@ int pa_paged_attention_decode(void* out, const void* q, const void* k_cache, con
     part_blocks = partition_size / kBlock;
     parts = std::max<int64_t>(1, ceil_div(max_len, partition_size));
   }
-  if (parts > INT_MAX) return PA_ERR_SHAPE;
+  if (parts > kMaxGridYZ) return PA_ERR_SHAPE;  // partitions are a grid dimension
 
   const WsLayout ws = ws_layout(num_seqs, num_q_heads, head_dim, parts);
   if (ws.total && (!workspace || workspace_bytes < ws.total)) return PA_ERR_WORKSPACE;
@@ -132,9 +135,10 @@ int pa_paged_attention_decode(void* out, const void* q, const void* k_cache, con
   a.block_tables = block_tables;
   a.context_lens = context_lens;
   char* wsb = static_cast<char*>(workspace);
-  a.tmp_out = ws.total ? reinterpret_cast<float*>(wsb + ws.tmp_out) : nullptr;
-  a.max_logits = ws.total ? reinterpret_cast<float*>(wsb + ws.max_logits) : nullptr;
-  a.exp_sums = ws.total ? reinterpret_cast<float*>(wsb + ws.exp_sums) : nullptr;
+  a.tmp_out = parts > 1 ? reinterpret_cast<float*>(wsb + ws.tmp_out) : nullptr;
+  a.max_logits = parts > 1 ? reinterpret_cast<float*>(wsb + ws.max_logits) : nullptr;
+  a.exp_sums = parts > 1 ? reinterpret_cast<float*>(wsb + ws.exp_sums) : nullptr;
+  a.num_seqs = num_seqs;
   a.num_blocks_i32 = (int)std::min<int64_t>(num_blocks, INT32_MAX);
   a.num_q_heads = num_q_heads;
   a.num_kv_heads = num_kv_heads;
@@ -148,9 +152,9 @@ int pa_paged_attention_decode(void* out, const void* q, const void* k_cache, con
   const int group = num_q_heads / num_kv_heads;
   // Grouped heads share every K/V tile: a matrix-core product pays off from
   // two heads up.  Single heads and fp32 stay on the vector ALU.
-  const bool use_mfma = dtype != PA_F32 && group >= 2;
-  hipError_t e = use_mfma ? pa::launch_decode_mfma(a, dtype, head_dim, num_seqs, st)
-                          : pa::launch_decode_valu(a, dtype, head_dim, num_seqs, st);
+  const bool use_mfma = dtype != PA_F32 && group >= PA_MFMA_MIN_GROUP;
+  hipError_t e = use_mfma ? pa::launch_decode_mfma(a, dtype, head_dim, st)
+                          : pa::launch_decode_valu(a, dtype, head_dim, st);
   if (e != hipSuccess) return PA_ERR_LAUNCH;
   if (parts > 1) {
     pa::ReduceArgs r{};

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace pa {
 
 enum Dtype : int { kF32 = 0, kF16 = 1, kBF16 = 2 };
@@ -112,6 +114,55 @@ __device__ __forceinline__ void axpy16(float p, const u32x4& v, float* acc) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---------------------------------------------------------------------------
+// buffer loads
+//
+// A tile is read through a buffer descriptor covering exactly its bytes.  A
+// descriptor with zero records makes every load through it return zeros
+// without touching memory, so loads can be issued unconditionally (no branch
+// around them -- which keeps the load counters exact) for tiles past the end
+// of a wave's work or with an invalid block id.
+
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+constexpr int kBufferWord3 = 0x00020000;  // raw 32-bit data format, no swizzle
+
+// Cache policy of the K/V tile loads (the instruction's cache-policy bits).
+// A private tile is read once per call, so it is loaded non-temporally (nt:
+// streamed past cache allocation, which measurably raises gather bandwidth).
+// A tile shared by several sequences (a common prefix) is re-read by each of
+// them and is loaded with the default, cache-allocating policy.
+#ifndef PA_KV_LOAD_POLICY
+#define PA_KV_LOAD_POLICY 2   // nt
+#endif
+#ifndef PA_SHARED_LOAD_POLICY
+#define PA_SHARED_LOAD_POLICY 0
+#endif
+
+__device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kBufferWord3);
+}
+template <bool SHARED = false>
+__device__ __forceinline__ u32x4 buf_load16(Rsrc r, uint32_t byte_off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(
+      r, (int)byte_off, 0, SHARED ? PA_SHARED_LOAD_POLICY : PA_KV_LOAD_POLICY);
+}
+template <bool SHARED = false>
+__device__ __forceinline__ u32x2 buf_load8(Rsrc r, uint32_t byte_off) {
+  return __builtin_amdgcn_raw_buffer_load_b64(
+      r, (int)byte_off, 0, SHARED ? PA_SHARED_LOAD_POLICY : PA_KV_LOAD_POLICY);
+}
+
+
+// f(integral_constant<int, I>) for I = B .. E-1, unrolled at compile time
+// (register arrays indexed by I stay in fixed registers).
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
 
 // ---------------------------------------------------------------------------
 // wave64 cross-lane reductions

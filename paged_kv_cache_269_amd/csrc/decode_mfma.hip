@@ -35,6 +35,7 @@
 #include <type_traits>
 
 #include "common.h"
+#include "items.h"
 #include "launch.h"
 
 namespace pa {
@@ -73,6 +74,8 @@ struct VSlice;
 template <>
 struct VSlice<8> {
   using T = u32x4;
+  template <bool SHARED>
+  __device__ static __forceinline__ T load(Rsrc r, int off) { return buf_load16<SHARED>(r, off); }
   __device__ static __forceinline__ uint32_t half(const T& v, int k) {
     return (k & 1) ? (v[k >> 1] >> 16) : (v[k >> 1] & 0xffffu);
   }
@@ -80,20 +83,30 @@ struct VSlice<8> {
 template <>
 struct VSlice<4> {
   using T = u32x2;
+  template <bool SHARED>
+  __device__ static __forceinline__ T load(Rsrc r, int off) { return buf_load8<SHARED>(r, off); }
   __device__ static __forceinline__ uint32_t half(const T& v, int k) {
     return (k & 1) ? (v[k >> 1] >> 16) : (v[k >> 1] & 0xffffu);
   }
 };
 
-template <int DT, int D, int NW>
-__global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
+template <int D, int NW>
+struct MfmaLds {
+  float m[NW][16], l[NW][16], f[NW][16], tot[16], mx[16];
+  float o[NW][16][D];
+};
+
+// One item: head tile hy (a KV head and up to 16 of its query heads) of
+// sequence s over partition `part` (context L).
+template <int DT, int D, int NW, int DEPTH>
+__device__ __forceinline__ void mfma_item(const DecodeArgs& a, const int hy, const int s,
+                                          const int part, const int L, MfmaLds<D, NW>& sm) {
   constexpr int NJ = D / 32;    // S products per block
   constexpr int EPL = D / 16;   // V elements per lane per row = PV products
   constexpr int CPR = D / 8;    // 16-byte chunks per row
   using VS = VSlice<EPL>;
   using VT = typename VS::T;
 
-  const int part = blockIdx.x, hy = blockIdx.y, s = blockIdx.z;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int n = lane & 15, g = lane >> 4;
@@ -102,12 +115,8 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
   const int kvh = hy / hchunks;
   const int head0 = kvh * group + (hy % hchunks) * 16;
   const int nh = min(16, kvh * group + group - head0);
-
-  int L = a.context_lens[s];
-  L = L < 0 ? 0 : (L > a.max_len ? a.max_len : L);
   const int nblocks = (L + kBlockSize - 1) / kBlockSize;
   const int nparts = (nblocks + a.part_blocks - 1) / a.part_blocks;
-  if (part > 0 && part >= nparts) return;
   const int64_t orow0 = (int64_t)s * a.num_q_heads + head0;
   if (L == 0) {
     for (int i = threadIdx.x; i < nh * D; i += NW * 64) store_elem<DT>(a.out, orow0 * D + i, 0.f);
@@ -124,12 +133,15 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
       qb[jj] = (n < nh) ? q[(orow0 + n) * CPR + 4 * jj + g] : u32x4{0u, 0u, 0u, 0u};
   }
 
-  const u32x4* __restrict__ kc = reinterpret_cast<const u32x4*>(a.k_cache);
-  const VT* __restrict__ vc = reinterpret_cast<const VT*>(a.v_cache);
+  constexpr int TILE_BYTES = kBlockSize * D * 2;
+  const char* kbase = static_cast<const char*>(a.k_cache);
+  const char* vbase = static_cast<const char*>(a.v_cache);
   const int32_t* __restrict__ bt = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
   const int jb = part * a.part_blocks;
   const int je = min(jb + a.part_blocks, nblocks);
-  const int tok_k = (n >> 2) + 4 * (n & 3);  // token of S row n
+  const int j0 = jb + w;                                  // this wave: blocks j0, j0+NW, ...
+  const int nk = je > j0 ? (je - j0 + NW - 1) / NW : 0;  // how many
+  const int tok_k = (n >> 2) + 4 * (n & 3);               // token of S row n
 
   float m = -INFINITY;   // running max of head n (base 2)
   float lsum = 0.f;      // this lane's share of head n's sum (tokens g + 4e)
@@ -137,21 +149,25 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
   for (int jj = 0; jj < EPL; ++jj) o[jj] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto locate = [&](int j, int bid, int& limit) -> int64_t {  // tile base in elements
-    limit = min(kBlockSize, L - j * kBlockSize);
-    if ((uint32_t)bid >= (uint32_t)a.num_blocks_i32) {  // not a pool block: skip its tokens
-      bid = 0;
-      limit = 0;
-    }
-    return ((int64_t)bid * a.num_kv_heads + kvh) * (kBlockSize * D);
+  // Pool id of the wave's kk-th block (index clamped into the table row).
+  auto id_at = [&](int kk) -> int { return bt[j0 + min(kk, nk - 1) * NW]; };
+  // Descriptors of the wave's kk-th tile and the number of its tokens in the
+  // context; empty past the wave's last block or for an id outside the pool.
+  auto tile = [&](int kk, int bid, int& limit, Rsrc& rk, Rsrc& rv) {
+    const int j = j0 + min(kk, nk - 1) * NW;
+    const bool ok = kk < nk && (uint32_t)bid < (uint32_t)a.num_blocks_i32;
+    limit = ok ? min(kBlockSize, L - j * kBlockSize) : 0;
+    const int64_t off = ((int64_t)(ok ? bid : 0) * a.num_kv_heads + kvh) * TILE_BYTES;
+    rk = make_rsrc(kbase + off, ok ? TILE_BYTES : 0);
+    rv = make_rsrc(vbase + off, ok ? TILE_BYTES : 0);
   };
-  auto load = [&](int64_t base, u32x4 (&kr)[NJ], VT (&vr)[4]) {
-    const u32x4* kt = kc + base / 8;
+  auto load = [&](auto shared, Rsrc rk, Rsrc rv, u32x4 (&kr)[NJ], VT (&vr)[4]) {
+    constexpr bool SH = decltype(shared)::value;
 #pragma unroll
-    for (int jj = 0; jj < NJ; ++jj) kr[jj] = kt[tok_k * CPR + 4 * jj + g];
-    const VT* vt = vc + base / EPL;
+    for (int jj = 0; jj < NJ; ++jj) kr[jj] = buf_load16<SH>(rk, (tok_k * CPR + 4 * jj + g) * 16);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) vr[e] = vt[(g + 4 * e) * 16 + n];
+    for (int e = 0; e < 4; ++e)
+      vr[e] = VS::template load<SH>(rv, ((g + 4 * e) * 16 + n) * (int)sizeof(VT));
   };
   auto consume = [&](auto masked, const u32x4 (&kr)[NJ], VT (&vr)[4], int limit) {
     constexpr bool MASKED = decltype(masked)::value;
@@ -208,97 +224,138 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
       consume(std::true_type{}, kr, vr, limit);
   };
 
-  // Ping-pong register sets: block k+1 loads in flight while block k is
-  // consumed; the pool id of block k+2 is fetched (scalar load) before that.
-  u32x4 kA[NJ], kB[NJ];
-  VT vA[4], vB[4];
-  const int j0 = jb + w;
-  const int nk = je > j0 ? (je - j0 + NW - 1) / NW : 0;
-  if (nk > 0) {
-    int id1 = nk > 1 ? bt[j0 + NW] : 0;
-    int limA, limB = 0;
-    load(locate(j0, bt[j0], limA), kA, vA);
-    for (int k = 0;; k += 2) {
-      const int id2 = k + 2 < nk ? bt[j0 + (k + 2) * NW] : 0;
-      if (k + 1 < nk) load(locate(j0 + (k + 1) * NW, id1, limB), kB, vB);
-      consume_block(kA, vA, limA);
-      if (k + 1 >= nk) break;
-      id1 = k + 3 < nk ? bt[j0 + (k + 3) * NW] : 0;
-      if (k + 2 < nk) load(locate(j0 + (k + 2) * NW, id2, limA), kA, vA);
-      consume_block(kB, vB, limB);
-      if (k + 2 >= nk) break;
+  // Software pipeline over the wave's blocks: DEPTH register sets; while
+  // block k is consumed, the loads of blocks k+1 .. k+DEPTH-1 are in flight,
+  // and the pool id of the next block to issue is already being fetched.
+  // Every step issues its loads (empty past the end) so that the wait counts
+  // are the same on every path -- no branch around a load -- and a
+  // past-the-end step consumes nothing.
+  u32x4 kr[DEPTH][NJ];
+  VT vr[DEPTH][4];
+  int lim[DEPTH];
+  auto pipeline = [&](auto shared) {
+    static_for<0, DEPTH - 1>([&](auto dc) {
+      constexpr int d = decltype(dc)::value;
+      Rsrc rk, rv;
+      tile(d, id_at(d), lim[d], rk, rv);
+      load(shared, rk, rv, kr[d], vr[d]);
+    });
+    int next_id = id_at(DEPTH - 1);
+    for (int k = 0; k < nk; k += DEPTH) {
+      static_for<0, DEPTH>([&](auto dc) {
+        constexpr int d = decltype(dc)::value;
+        constexpr int dn = (d + DEPTH - 1) % DEPTH;
+        const int kn = k + d + DEPTH - 1;  // block whose loads are issued now
+        const int id = next_id;
+        next_id = id_at(kn + 1);
+        Rsrc rk, rv;
+        tile(kn, id, lim[dn], rk, rv);
+        load(shared, rk, rv, kr[dn], vr[dn]);
+        consume_block(kr[d], vr[d], lim[d]);
+      });
     }
+  };
+  if (nk > 0) {
+    // Shared prefix pages are re-read by every sequence that maps them: an
+    // item whose first block the neighbouring sequence's table maps to the
+    // same physical block loads with the cache-allocating policy; all other
+    // items stream their tiles non-temporally.
+    const int32_t* nb = a.num_seqs > 1 ? a.block_tables +
+                            (int64_t)(s > 0 ? s - 1 : s + 1) * a.max_blocks_per_seq : nullptr;
+    if (nb != nullptr && nb[j0] == bt[j0])
+      pipeline(std::true_type{});
+    else
+      pipeline(std::false_type{});
   }
 
   // Per-head totals of this wave, then the cross-wave merge through LDS.
   lsum = xor16_combine(lsum, AddOp{});
   lsum = xor32_combine(lsum, AddOp{});
-  __shared__ float s_m[NW][16], s_l[NW][16], s_f[NW][16], s_tot[16], s_max[16];
-  __shared__ float s_o[NW][16][D];
   if (g == 0) {
-    s_m[w][n] = m;
-    s_l[w][n] = lsum;
+    sm.m[w][n] = m;
+    sm.l[w][n] = lsum;
   }
 #pragma unroll
   for (int e = 0; e < 4; ++e)
 #pragma unroll
-    for (int jj = 0; jj < EPL; ++jj) s_o[w][4 * g + e][EPL * n + jj] = o[jj][e];
+    for (int jj = 0; jj < EPL; ++jj) sm.o[w][4 * g + e][EPL * n + jj] = o[jj][e];
   __syncthreads();
   if (threadIdx.x < 16) {
     const int hh = threadIdx.x;
     float M = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < NW; ++i) M = __builtin_fmaxf(M, s_m[i][hh]);
+    for (int i = 0; i < NW; ++i) M = __builtin_fmaxf(M, sm.m[i][hh]);
     float tot = 0.f;
     float f[NW];
 #pragma unroll
     for (int i = 0; i < NW; ++i) {
-      f[i] = (s_m[i][hh] == -INFINITY) ? 0.f : fast_exp2(s_m[i][hh] - M);
-      tot += s_l[i][hh] * f[i];
+      f[i] = (sm.m[i][hh] == -INFINITY) ? 0.f : fast_exp2(sm.m[i][hh] - M);
+      tot += sm.l[i][hh] * f[i];
     }
     const float inv = tot > 0.f ? 1.f / tot : 0.f;
 #pragma unroll
-    for (int i = 0; i < NW; ++i) s_f[i][hh] = f[i] * inv;
-    s_tot[hh] = tot;
-    s_max[hh] = M;
+    for (int i = 0; i < NW; ++i) sm.f[i][hh] = f[i] * inv;
+    sm.tot[hh] = tot;
+    sm.mx[hh] = M;
   }
   __syncthreads();
   for (int i = threadIdx.x; i < nh * D; i += NW * 64) {
     const int hh = i / D, d = i % D;
     float v = 0.f;
 #pragma unroll
-    for (int k = 0; k < NW; ++k) v += s_o[k][hh][d] * s_f[k][hh];
+    for (int k = 0; k < NW; ++k) v += sm.o[k][hh][d] * sm.f[k][hh];
     if (nparts <= 1) {
       store_elem<DT>(a.out, (orow0 + hh) * D + d, v);
     } else {
       const int64_t prow = (orow0 + hh) * a.max_partitions + part;
       a.tmp_out[prow * D + d] = v;
       if (d == 0) {
-        a.max_logits[prow] = s_max[hh] * kLn2;
-        a.exp_sums[prow] = s_tot[hh];
+        a.max_logits[prow] = sm.mx[hh] * kLn2;
+        a.exp_sums[prow] = sm.tot[hh];
       }
     }
   }
 }
 
-template <int DT, int D>
-hipError_t launch_typed(const DecodeArgs& a, int num_seqs, hipStream_t stream) {
-  constexpr int NW = 4;
+// One workgroup per item.  Head units vary fastest across the grid:
+// workgroups are dealt to the 8 XCDs round-robin, so the equal-sized items of
+// one (sequence, partition) spread evenly over the XCDs, and one head unit of
+// every sequence stays on one XCD (shared prefix pages then hit its L2).
+template <int DT, int D, int NW, int DEPTH>
+__global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
+  __shared__ MfmaLds<D, NW> sm;
+  const int unit = blockIdx.x, s = blockIdx.y, part = blockIdx.z;
+  const int L = clamp_len(a, s);
+  if (part >= parts_of(L, a.part_blocks)) return;  // past this sequence's end
+  mfma_item<DT, D, NW, DEPTH>(a, unit, s, part, L, sm);
+}
+
+// Launch shapes: items of at least kLongItemBlocks blocks get 8 waves,
+// shorter ones 4 (more workgroups resident per CU).
+constexpr int kLongItemBlocks = 128;
+
+template <int DT, int D, int NW, int DEPTH>
+hipError_t launch_shape(const DecodeArgs& a, hipStream_t stream) {
   const int group = a.num_q_heads / a.num_kv_heads;
-  dim3 grid(a.max_partitions, a.num_kv_heads * ((group + 15) / 16), num_seqs);
-  hipLaunchKernelGGL((decode_mfma_kernel<DT, D, NW>), grid, dim3(NW * 64), 0, stream, a);
+  const dim3 grid(a.num_kv_heads * ((group + 15) / 16), a.num_seqs, a.max_partitions);
+  hipLaunchKernelGGL((decode_mfma_kernel<DT, D, NW, DEPTH>), grid, dim3(NW * 64), 0, stream, a);
   return hipGetLastError();
+}
+
+template <int DT, int D>
+hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
+  return a.part_blocks >= kLongItemBlocks ? launch_shape<DT, D, 8, 2>(a, stream)
+                                          : launch_shape<DT, D, 4, 2>(a, stream);
 }
 
 }  // namespace
 
-hipError_t launch_decode_mfma(const DecodeArgs& a, int dtype, int head_dim, int num_seqs,
-                              hipStream_t stream) {
+hipError_t launch_decode_mfma(const DecodeArgs& a, int dtype, int head_dim, hipStream_t stream) {
   switch (dtype * 1000 + head_dim) {
-    case kF16 * 1000 + 64: return launch_typed<kF16, 64>(a, num_seqs, stream);
-    case kF16 * 1000 + 128: return launch_typed<kF16, 128>(a, num_seqs, stream);
-    case kBF16 * 1000 + 64: return launch_typed<kBF16, 64>(a, num_seqs, stream);
-    case kBF16 * 1000 + 128: return launch_typed<kBF16, 128>(a, num_seqs, stream);
+    case kF16 * 1000 + 64: return launch_typed<kF16, 64>(a, stream);
+    case kF16 * 1000 + 128: return launch_typed<kF16, 128>(a, stream);
+    case kBF16 * 1000 + 64: return launch_typed<kBF16, 64>(a, stream);
+    case kBF16 * 1000 + 128: return launch_typed<kBF16, 128>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }

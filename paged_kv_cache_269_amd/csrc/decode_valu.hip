@@ -9,7 +9,7 @@
 // fused kernel, wide vector loads.
 //
 // Work split (gfx950, wave64):
-//   workgroup = (partition, query head, sequence), NW waves;
+//   workgroup = (query head, sequence, partition), NW waves;
 //   wave w takes blocks w, w+NW, ... of its partition;
 //   one (block, kv head) tile is 16 rows of head_dim elements, contiguous in
 //   HBM (16 * D * e bytes).  A wave-wide 16-byte-per-lane load covers TPL =
@@ -29,6 +29,7 @@
 #include <type_traits>
 
 #include "common.h"
+#include "items.h"
 #include "launch.h"
 
 namespace pa {
@@ -41,27 +42,32 @@ struct ValuShape {
   static constexpr int LPT = D / VEC;               // lanes per token row
   static constexpr int TPL = 64 / LPT;              // token rows per wave load
   static constexpr int NLD = kBlockSize / TPL;      // loads per tile per lane
-  static constexpr int CPT = kBlockSize * D / VEC;  // 16-byte chunks per tile
+  static constexpr int TILE_BYTES = kBlockSize * D * Elem<DT>::bytes;  // one (block, head) tile
   static_assert(LPT >= 2 && LPT <= 32 && TPL * LPT == 64, "unsupported head_dim");
 };
 
+// Shared memory of one workgroup: the per-row partial states of an item.
 template <int DT, int D, int NW>
-__global__ __launch_bounds__(NW * 64) void decode_valu_kernel(DecodeArgs a) {
+struct ValuLds {
+  static constexpr int R = NW * ValuShape<DT, D>::TPL;
+  float m[R], l[R];
+  float acc[R * D];
+};
+
+// One item: query head h of sequence s over partition `part` (context L).
+template <int DT, int D, int NW, int DEPTH>
+__device__ __forceinline__ void valu_item(const DecodeArgs& a, const int h, const int s,
+                                          const int part, const int L, ValuLds<DT, D, NW>& sm) {
   using S = ValuShape<DT, D>;
   constexpr int VEC = S::VEC, LPT = S::LPT, TPL = S::TPL, NLD = S::NLD;
 
-  const int part = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int row = lane / LPT, c = lane % LPT;
   const int group = a.num_q_heads / a.num_kv_heads;
   const int kvh = h / group;
-
-  int L = a.context_lens[s];
-  L = L < 0 ? 0 : (L > a.max_len ? a.max_len : L);
   const int nblocks = (L + kBlockSize - 1) / kBlockSize;
   const int nparts = (nblocks + a.part_blocks - 1) / a.part_blocks;
-  if (part > 0 && part >= nparts) return;
   const int64_t orow = (int64_t)s * a.num_q_heads + h;
   if (L == 0) {
     for (int d = threadIdx.x; d < D; d += NW * 64) store_elem<DT>(a.out, orow * D + d, 0.f);
@@ -69,32 +75,38 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(DecodeArgs a) {
   }
 
   const u32x4 qv = reinterpret_cast<const u32x4*>(a.q)[orow * (D / VEC) + c];
-  const u32x4* __restrict__ kc = reinterpret_cast<const u32x4*>(a.k_cache);
-  const u32x4* __restrict__ vc = reinterpret_cast<const u32x4*>(a.v_cache);
+  const char* kbase = static_cast<const char*>(a.k_cache);
+  const char* vbase = static_cast<const char*>(a.v_cache);
   const int32_t* __restrict__ bt = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
   const int jb = part * a.part_blocks;
   const int je = min(jb + a.part_blocks, nblocks);
+  const int j0 = jb + w;                                  // this wave: blocks j0, j0+NW, ...
+  const int nk = je > j0 ? (je - j0 + NW - 1) / NW : 0;  // how many
 
   float m = -INFINITY, l = 0.f;
   float acc[VEC];
 #pragma unroll
   for (int k = 0; k < VEC; ++k) acc[k] = 0.f;
 
-  // Tile base (in 16-byte chunks) of block j whose pool id is bid, and the
-  // number of its tokens that belong to the context.
-  auto locate = [&](int j, int bid, int& limit) -> int64_t {
-    limit = min(kBlockSize, L - j * kBlockSize);
-    if ((uint32_t)bid >= (uint32_t)a.num_blocks_i32) {  // not a pool block: skip its tokens
-      bid = 0;
-      limit = 0;
-    }
-    return ((int64_t)bid * a.num_kv_heads + kvh) * S::CPT;
+  // Pool id of the wave's kk-th block (index clamped into the table row).
+  auto id_at = [&](int kk) -> int { return bt[j0 + min(kk, nk - 1) * NW]; };
+  // Descriptors of the wave's kk-th tile and the number of its tokens in the
+  // context; past the wave's last block, or for an id outside the pool, the
+  // descriptors are empty and no token counts.
+  auto tile = [&](int kk, int bid, int& limit, Rsrc& rk, Rsrc& rv) {
+    const int j = j0 + min(kk, nk - 1) * NW;
+    const bool ok = kk < nk && (uint32_t)bid < (uint32_t)a.num_blocks_i32;
+    limit = ok ? min(kBlockSize, L - j * kBlockSize) : 0;
+    const int64_t off = ((int64_t)(ok ? bid : 0) * a.num_kv_heads + kvh) * S::TILE_BYTES;
+    rk = make_rsrc(kbase + off, ok ? S::TILE_BYTES : 0);
+    rv = make_rsrc(vbase + off, ok ? S::TILE_BYTES : 0);
   };
-  auto load = [&](int64_t base, u32x4 (&kr)[NLD], u32x4 (&vr)[NLD]) {
+  auto load = [&](auto shared, Rsrc rk, Rsrc rv, u32x4 (&kr)[NLD], u32x4 (&vr)[NLD]) {
+    constexpr bool SH = decltype(shared)::value;
 #pragma unroll
-    for (int i = 0; i < NLD; ++i) kr[i] = kc[base + i * 64 + lane];
+    for (int i = 0; i < NLD; ++i) kr[i] = buf_load16<SH>(rk, (i * 64 + lane) * 16);
 #pragma unroll
-    for (int i = 0; i < NLD; ++i) vr[i] = vc[base + i * 64 + lane];
+    for (int i = 0; i < NLD; ++i) vr[i] = buf_load16<SH>(rv, (i * 64 + lane) * 16);
   };
   auto consume = [&](auto masked, const u32x4 (&kr)[NLD], const u32x4 (&vr)[NLD], int limit) {
     constexpr bool MASKED = decltype(masked)::value;
@@ -135,51 +147,70 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(DecodeArgs a) {
       consume(std::true_type{}, kr, vr, limit);
   };
 
-  // Two register sets, ping-pong: the loads of block k+1 are in flight while
-  // block k is consumed, and the pool id of block k+2 is fetched (scalar
-  // load) before block k is consumed.
-  u32x4 kA[NLD], vA[NLD], kB[NLD], vB[NLD];
-  const int j0 = jb + w;
-  const int nk = je > j0 ? (je - j0 + NW - 1) / NW : 0;
-  if (nk > 0) {
-    int id1 = nk > 1 ? bt[j0 + NW] : 0;
-    int limA, limB = 0;
-    load(locate(j0, bt[j0], limA), kA, vA);
-    for (int k = 0;; k += 2) {
-      const int id2 = k + 2 < nk ? bt[j0 + (k + 2) * NW] : 0;
-      if (k + 1 < nk) load(locate(j0 + (k + 1) * NW, id1, limB), kB, vB);
-      consume_block(kA, vA, limA);
-      if (k + 1 >= nk) break;
-      id1 = k + 3 < nk ? bt[j0 + (k + 3) * NW] : 0;
-      if (k + 2 < nk) load(locate(j0 + (k + 2) * NW, id2, limA), kA, vA);
-      consume_block(kB, vB, limB);
-      if (k + 2 >= nk) break;
+  // Software pipeline over the wave's blocks: DEPTH register sets; while
+  // block k is consumed, the loads of blocks k+1 .. k+DEPTH-1 are in flight,
+  // and the pool id of the next block to issue is already being fetched.
+  // Every step issues its loads (empty past the end) so that the wait counts
+  // are the same on every path -- no branch around a load -- and a
+  // past-the-end step consumes nothing.
+  u32x4 kr[DEPTH][NLD], vr[DEPTH][NLD];
+  int lim[DEPTH];
+  auto pipeline = [&](auto shared) {
+    static_for<0, DEPTH - 1>([&](auto dc) {
+      constexpr int d = decltype(dc)::value;
+      Rsrc rk, rv;
+      tile(d, id_at(d), lim[d], rk, rv);
+      load(shared, rk, rv, kr[d], vr[d]);
+    });
+    int next_id = id_at(DEPTH - 1);
+    for (int k = 0; k < nk; k += DEPTH) {
+      static_for<0, DEPTH>([&](auto dc) {
+        constexpr int d = decltype(dc)::value;
+        constexpr int dn = (d + DEPTH - 1) % DEPTH;
+        const int kn = k + d + DEPTH - 1;  // block whose loads are issued now
+        const int id = next_id;
+        next_id = id_at(kn + 1);
+        Rsrc rk, rv;
+        tile(kn, id, lim[dn], rk, rv);
+        load(shared, rk, rv, kr[dn], vr[dn]);
+        consume_block(kr[d], vr[d], lim[d]);
+      });
     }
+  };
+  if (nk > 0) {
+    // Shared prefix pages are re-read by every sequence that maps them: an
+    // item whose first block the neighbouring sequence's table maps to the
+    // same physical block loads with the cache-allocating policy; all other
+    // items stream their tiles non-temporally.
+    const int32_t* nb = a.num_seqs > 1 ? a.block_tables +
+                            (int64_t)(s > 0 ? s - 1 : s + 1) * a.max_blocks_per_seq : nullptr;
+    if (nb != nullptr && nb[j0] == bt[j0])
+      pipeline(std::true_type{});
+    else
+      pipeline(std::false_type{});
   }
 
   // Merge the TPL x NW partial states of this partition.
   constexpr int R = NW * TPL;
-  __shared__ float s_m[R], s_l[R];
-  __shared__ float s_acc[R * D];
   const int r = w * TPL + row;
   if (c == 0) {
-    s_m[r] = m;
-    s_l[r] = l;
+    sm.m[r] = m;
+    sm.l[r] = l;
   }
 #pragma unroll
-  for (int k = 0; k < VEC; ++k) s_acc[r * D + c * VEC + k] = acc[k];
+  for (int k = 0; k < VEC; ++k) sm.acc[r * D + c * VEC + k] = acc[k];
   __syncthreads();
 
   for (int d = threadIdx.x; d < D; d += NW * 64) {
     float M = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < R; ++i) M = __builtin_fmaxf(M, s_m[i]);
+    for (int i = 0; i < R; ++i) M = __builtin_fmaxf(M, sm.m[i]);
     float lsum = 0.f, o = 0.f;
 #pragma unroll
     for (int i = 0; i < R; ++i) {
-      const float f = (s_m[i] == -INFINITY) ? 0.f : fast_exp2(s_m[i] - M);
-      lsum += s_l[i] * f;
-      o += s_acc[i * D + d] * f;
+      const float f = (sm.m[i] == -INFINITY) ? 0.f : fast_exp2(sm.m[i] - M);
+      lsum += sm.l[i] * f;
+      o += sm.acc[i * D + d] * f;
     }
     o = lsum > 0.f ? o / lsum : 0.f;
     if (nparts <= 1) {
@@ -195,25 +226,47 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(DecodeArgs a) {
   }
 }
 
-template <int DT, int D>
-hipError_t launch_typed(const DecodeArgs& a, int num_seqs, hipStream_t stream) {
-  constexpr int NW = 4;
-  dim3 grid(a.max_partitions, a.num_q_heads, num_seqs);
-  hipLaunchKernelGGL((decode_valu_kernel<DT, D, NW>), grid, dim3(NW * 64), 0, stream, a);
+// One workgroup per item.  Head units vary fastest across the grid:
+// workgroups are dealt to the 8 XCDs round-robin, so the equal-sized items of
+// one (sequence, partition) spread evenly over the XCDs, and one head unit of
+// every sequence stays on one XCD (shared prefix pages then hit its L2).
+template <int DT, int D, int NW, int DEPTH>
+__global__ __launch_bounds__(NW * 64) void decode_valu_kernel(DecodeArgs a) {
+  __shared__ ValuLds<DT, D, NW> sm;
+  const int unit = blockIdx.x, s = blockIdx.y, part = blockIdx.z;
+  const int L = clamp_len(a, s);
+  if (part >= parts_of(L, a.part_blocks)) return;  // past this sequence's end
+  valu_item<DT, D, NW, DEPTH>(a, unit, s, part, L, sm);
+}
+
+// Launch shapes: items of at least kLongItemBlocks blocks get 8 waves and a
+// 3-deep load pipeline (more bytes in flight per item); shorter items get 4
+// waves and 2 tiles in flight, which keeps more workgroups resident per CU.
+constexpr int kLongItemBlocks = 128;
+
+template <int DT, int D, int NW, int DEPTH>
+hipError_t launch_shape(const DecodeArgs& a, hipStream_t stream) {
+  const dim3 grid(a.num_q_heads, a.num_seqs, a.max_partitions);
+  hipLaunchKernelGGL((decode_valu_kernel<DT, D, NW, DEPTH>), grid, dim3(NW * 64), 0, stream, a);
   return hipGetLastError();
+}
+
+template <int DT, int D>
+hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
+  return a.part_blocks >= kLongItemBlocks ? launch_shape<DT, D, 8, 3>(a, stream)
+                                          : launch_shape<DT, D, 4, 2>(a, stream);
 }
 
 }  // namespace
 
-hipError_t launch_decode_valu(const DecodeArgs& a, int dtype, int head_dim, int num_seqs,
-                              hipStream_t stream) {
+hipError_t launch_decode_valu(const DecodeArgs& a, int dtype, int head_dim, hipStream_t stream) {
   switch (dtype * 1000 + head_dim) {
-    case kF32 * 1000 + 64: return launch_typed<kF32, 64>(a, num_seqs, stream);
-    case kF32 * 1000 + 128: return launch_typed<kF32, 128>(a, num_seqs, stream);
-    case kF16 * 1000 + 64: return launch_typed<kF16, 64>(a, num_seqs, stream);
-    case kF16 * 1000 + 128: return launch_typed<kF16, 128>(a, num_seqs, stream);
-    case kBF16 * 1000 + 64: return launch_typed<kBF16, 64>(a, num_seqs, stream);
-    case kBF16 * 1000 + 128: return launch_typed<kBF16, 128>(a, num_seqs, stream);
+    case kF32 * 1000 + 64: return launch_typed<kF32, 64>(a, stream);
+    case kF32 * 1000 + 128: return launch_typed<kF32, 128>(a, stream);
+    case kF16 * 1000 + 64: return launch_typed<kF16, 64>(a, stream);
+    case kF16 * 1000 + 128: return launch_typed<kF16, 128>(a, stream);
+    case kBF16 * 1000 + 64: return launch_typed<kBF16, 64>(a, stream);
+    case kBF16 * 1000 + 128: return launch_typed<kBF16, 128>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -17,13 +17,14 @@ struct DecodeArgs {
   float* tmp_out;               // [B, Hq, P, D] partial outputs (normalised)
   float* max_logits;            // [B, Hq, P]  (natural-log units)
   float* exp_sums;              // [B, Hq, P]
+  int num_seqs;                 // B
   int num_blocks_i32;           // N, clamped to INT32_MAX (block ids are int32)
   int num_q_heads;              // Hq
   int num_kv_heads;             // Hkv
   int max_blocks_per_seq;       // M
   int max_len;                  // contexts are clamped to [0, max_len]
   int part_blocks;              // blocks per partition
-  int max_partitions;           // P (grid x)
+  int max_partitions;           // P (partials stride)
   float scale_log2;             // scale * log2(e)
 };
 
@@ -45,14 +46,12 @@ hipError_t launch_reshape_and_cache(const void* key, const void* value, void* k_
                                     int num_kv_heads, int head_dim, int elem_bytes,
                                     int64_t num_blocks, hipStream_t stream);
 
-// Vector-ALU decode: one workgroup per (partition, query head, sequence).
-hipError_t launch_decode_valu(const DecodeArgs& a, int dtype, int head_dim, int num_seqs,
-                              hipStream_t stream);
+// Vector-ALU decode: one workgroup per (query head, sequence, partition) item.
+hipError_t launch_decode_valu(const DecodeArgs& a, int dtype, int head_dim, hipStream_t stream);
 
-// Matrix-core decode for grouped heads: one workgroup per (partition,
-// kv head x 16-head chunk, sequence).
-hipError_t launch_decode_mfma(const DecodeArgs& a, int dtype, int head_dim, int num_seqs,
-                              hipStream_t stream);
+// Matrix-core decode for grouped heads: one workgroup per (kv head x 16-head
+// tile, sequence, partition) item.
+hipError_t launch_decode_mfma(const DecodeArgs& a, int dtype, int head_dim, hipStream_t stream);
 
 hipError_t launch_reduce(const ReduceArgs& a, int dtype, int head_dim, int num_seqs,
                          hipStream_t stream);

@@ -82,6 +82,7 @@ def test_workspace_bytes(hiplib):
     assert f(-1, 8, 128, 513, 512) == 0
 
 
+
 def test_reshape_and_reduce_argument_checks(hiplib):
     lib = hiplib.load_library()
     r = lib.pa_reshape_and_cache

@@ -60,7 +60,7 @@ def test_small_configs_full_parity(cuda, name):
     run.oracle_reshape()
     pool_equal(run, w)
     ref = full_oracle(w)
-    for part in sorted({w.partition_size, 0, 16}):
+    for part in sorted({w.partition_size, 0, 16, 512}):
         out = run.decode(partition_size=part)
         got = to_f64(tensor_to_np(out, w.dtype), w.dtype)
         stats = check_close(got, ref, w.dtype, f"{name} partition {part}")
@@ -119,7 +119,7 @@ def test_edge_lengths_and_partitions(cuda, dtype, D, G):
     run.oracle_reshape()
     pool_equal(run, w)
     ref = full_oracle(w)
-    for part in (0, 16, 256, 512):
+    for part in (0, 16, 256, 512, 2048):
         out = run.decode(partition_size=part)
         got_raw = tensor_to_np(out, dtype)
         got = to_f64(got_raw, dtype)
