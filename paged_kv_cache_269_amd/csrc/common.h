@@ -172,6 +172,7 @@ constexpr int kDppQuadXor1 = 0xB1;   // quad_perm [1,0,3,2]
 constexpr int kDppQuadXor2 = 0x4E;   // quad_perm [2,3,0,1]
 constexpr int kDppRowMirror = 0x140; // lane i <-> 15 - i within a row
 constexpr int kDppHalfMirror = 0x141;// lane i <-> 7 - i within each half row
+constexpr int kDppRowRor8 = 0x128;   // lane i <-> i ^ 8 within a row (rotate by 8)
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
@@ -220,6 +221,33 @@ __device__ __forceinline__ float group_reduce(float x, Op op) {
 template <int N>
 __device__ __forceinline__ float group_sum(float x) {
   return group_reduce<N>(x, AddOp{});
+}
+
+// Reduction across the 64 / N aligned groups of N lanes: every lane receives
+// op over all lanes with the same index within their group (N in {8,16,32}).
+template <int N, typename Op>
+__device__ __forceinline__ float across_groups(float x, Op op) {
+  static_assert(N == 8 || N == 16 || N == 32, "group size");
+  if constexpr (N == 8) x = op(x, dpp<kDppRowRor8>(x));
+  if constexpr (N <= 16) x = xor16_combine(x, op);
+  x = xor32_combine(x, op);
+  return x;
+}
+
+// Store n = 4 (fp32) or 8 (fp16/bf16) consecutive results as one 16-byte
+// store; base + idx must be 16-byte aligned.
+template <int DT>
+__device__ __forceinline__ void store16(void* base, int64_t idx, const float* v) {
+  if constexpr (DT == kF32) {
+    *reinterpret_cast<u32x4*>(reinterpret_cast<float*>(base) + idx) =
+        u32x4{f2u(v[0]), f2u(v[1]), f2u(v[2]), f2u(v[3])};
+  } else {
+    u32x4 w;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      w[k] = (uint32_t)to_bits16<DT>(v[2 * k]) | ((uint32_t)to_bits16<DT>(v[2 * k + 1]) << 16);
+    *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(base) + idx) = w;
+  }
 }
 
 }  // namespace pa

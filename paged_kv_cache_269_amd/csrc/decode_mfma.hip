@@ -96,132 +96,241 @@ struct MfmaLds {
   float o[NW][16][D];
 };
 
-// One item: head tile hy (a KV head and up to 16 of its query heads) of
-// sequence s over partition `part` (context L).
-template <int DT, int D, int NW, int DEPTH>
-__device__ __forceinline__ void mfma_item(const DecodeArgs& a, const int hy, const int s,
-                                          const int part, const int L, MfmaLds<D, NW>& sm) {
-  constexpr int NJ = D / 32;    // S products per block
-  constexpr int EPL = D / 16;   // V elements per lane per row = PV products
-  constexpr int CPR = D / 8;    // 16-byte chunks per row
+// Shapes of one (block, KV head) tile for the matrix-core path.
+template <int DT, int D>
+struct MfmaShape {
+  static constexpr int NJ = D / 32;   // S products per block
+  static constexpr int EPL = D / 16;  // V elements per lane per row = PV products
+  static constexpr int CPR = D / 8;   // 16-byte chunks per row
+  static constexpr int TILE_BYTES = kBlockSize * D * 2;
   using VS = VSlice<EPL>;
   using VT = typename VS::T;
+};
 
-  const int lane = threadIdx.x & 63;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
-  const int n = lane & 15, g = lane >> 4;
+// Lane coordinates inside the wave.
+struct MfmaLane {
+  int n, g, tok_k;  // column/row n, contraction slice g, token of S row n
+  __device__ __forceinline__ MfmaLane() {
+    const int lane = threadIdx.x & 63;
+    n = lane & 15;
+    g = lane >> 4;
+    tok_k = (n >> 2) + 4 * (n & 3);
+  }
+};
+
+// Softmax state of one wave for one item: running max of head n (base 2),
+// this lane's share of head n's sum (tokens g + 4e), P.V accumulators
+// (rows = heads 4g..4g+3, column n = dim EPL*n + jj).
+template <int D>
+struct MfmaState {
+  float m, lsum;
+  f32x4 o[D / 16];
+  __device__ __forceinline__ void reset() {
+    m = -INFINITY;
+    lsum = 0.f;
+#pragma unroll
+    for (int jj = 0; jj < D / 16; ++jj) o[jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+};
+
+// Head tile of an item: KV head and its first query head / count.
+struct HeadTile {
+  int kvh, nh;
+  int64_t orow0;  // (s, first query head) row index
+};
+
+__device__ __forceinline__ HeadTile head_tile(const DecodeArgs& a, int unit, int s) {
   const int group = a.num_q_heads / a.num_kv_heads;
   const int hchunks = (group + 15) >> 4;
-  const int kvh = hy / hchunks;
-  const int head0 = kvh * group + (hy % hchunks) * 16;
-  const int nh = min(16, kvh * group + group - head0);
+  HeadTile t;
+  t.kvh = unit / hchunks;
+  const int head0 = t.kvh * group + (unit % hchunks) * 16;
+  t.nh = min(16, t.kvh * group + group - head0);
+  t.orow0 = (int64_t)s * a.num_q_heads + head0;
+  return t;
+}
+
+// Q^T as the B operand of the S products: column n = head n, slice g of
+// product j = chunk 4j + g of the head's row.  Idle heads read nothing.
+template <int DT, int D>
+__device__ __forceinline__ void load_q(const DecodeArgs& a, const HeadTile& t, const MfmaLane& ln,
+                                       u32x4 (&qb)[D / 32]) {
+  using S = MfmaShape<DT, D>;
+  const u32x4* q = reinterpret_cast<const u32x4*>(a.q);
+#pragma unroll
+  for (int jj = 0; jj < S::NJ; ++jj)
+    qb[jj] = (ln.n < t.nh) ? q[(t.orow0 + ln.n) * S::CPR + 4 * jj + ln.g] : u32x4{0u, 0u, 0u, 0u};
+}
+
+// Descriptors of the tile of pool block `bid` for KV head kvh; empty when
+// !ok (loads through them return zeros without touching memory).
+template <int DT, int D>
+__device__ __forceinline__ void tile_rsrc(const DecodeArgs& a, int bid, int kvh, bool ok, Rsrc& rk,
+                                          Rsrc& rv) {
+  using S = MfmaShape<DT, D>;
+  ok = ok && (uint32_t)bid < (uint32_t)a.num_blocks_i32;
+  const int64_t off = ((int64_t)(ok ? bid : 0) * a.num_kv_heads + kvh) * S::TILE_BYTES;
+  rk = make_rsrc(static_cast<const char*>(a.k_cache) + off, ok ? S::TILE_BYTES : 0);
+  rv = make_rsrc(static_cast<const char*>(a.v_cache) + off, ok ? S::TILE_BYTES : 0);
+}
+
+// The lane's share of one tile: K rows tau(n) (A operand of S), V rows g+4e.
+template <int DT, int D, bool SH>
+__device__ __forceinline__ void load_tile(Rsrc rk, Rsrc rv, const MfmaLane& ln,
+                                          u32x4 (&kr)[D / 32],
+                                          typename MfmaShape<DT, D>::VT (&vr)[4]) {
+  using S = MfmaShape<DT, D>;
+#pragma unroll
+  for (int jj = 0; jj < S::NJ; ++jj)
+    kr[jj] = buf_load16<SH>(rk, (ln.tok_k * S::CPR + 4 * jj + ln.g) * 16);
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    vr[e] = S::VS::template load<SH>(rv, ((ln.g + 4 * e) * 16 + ln.n) *
+                                             (int)sizeof(typename S::VT));
+}
+
+// Fold one tile (`limit` of its 16 tokens in the context) into the state.
+template <int DT, int D, bool MASKED>
+__device__ __forceinline__ void consume_tile(MfmaState<D>& st, const u32x4 (&qb)[D / 32],
+                                             const u32x4 (&kr)[D / 32],
+                                             typename MfmaShape<DT, D>::VT (&vr)[4], int limit,
+                                             float scale_log2, const MfmaLane& ln) {
+  using S = MfmaShape<DT, D>;
+  using VT = typename S::VT;
+  f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int jj = 0; jj < S::NJ; ++jj) sacc = mfma_qk<DT>(kr[jj], qb[jj], sacc);
+  float sc[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    sc[e] = sacc[e] * scale_log2;
+    if constexpr (MASKED) {
+      const bool ok = ln.g + 4 * e < limit;
+      sc[e] = ok ? sc[e] : -INFINITY;
+      if (!ok) vr[e] = VT{};  // whatever the slot holds must not reach P.V
+    }
+  }
+  float mb = __builtin_fmaxf(__builtin_fmaxf(sc[0], sc[1]), __builtin_fmaxf(sc[2], sc[3]));
+  mb = xor16_combine(mb, MaxOp{});
+  mb = xor32_combine(mb, MaxOp{});
+  const float mn = __builtin_fmaxf(st.m, mb);
+  float alpha = fast_exp2(st.m - mn);
+  float p[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) p[e] = fast_exp2(sc[e] - mn);
+  if constexpr (MASKED) {
+    if (mn == -INFINITY) {  // no valid token of this head so far
+      alpha = 1.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) p[e] = 0.f;
+    }
+  }
+  st.lsum = st.lsum * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
+  st.m = mn;
+  // output rows 4g .. 4g+3 are heads 4g+e: fetch their factors
+  float arow[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    arow[e] = u2f((uint32_t)__builtin_amdgcn_ds_bpermute((4 * ln.g + e) << 2, (int)f2u(alpha)));
+  const u32x2 pa{pack2<DT>(p[0], p[1]), pack2<DT>(p[2], p[3])};
+#pragma unroll
+  for (int jj = 0; jj < S::EPL; ++jj) {
+    const u32x2 vb{S::VS::half(vr[0], jj) | (S::VS::half(vr[1], jj) << 16),
+                   S::VS::half(vr[2], jj) | (S::VS::half(vr[3], jj) << 16)};
+    f32x4 c = st.o[jj];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) c[e] *= arow[e];
+    st.o[jj] = mfma_pv<DT>(pa, vb, c);
+  }
+}
+
+template <int DT, int D>
+__device__ __forceinline__ void consume_any(MfmaState<D>& st, const u32x4 (&qb)[D / 32],
+                                            const u32x4 (&kr)[D / 32],
+                                            typename MfmaShape<DT, D>::VT (&vr)[4], int limit,
+                                            float scale_log2, const MfmaLane& ln) {
+  if (limit == kBlockSize)
+    consume_tile<DT, D, false>(st, qb, kr, vr, limit, scale_log2, ln);
+  else
+    consume_tile<DT, D, true>(st, qb, kr, vr, limit, scale_log2, ln);
+}
+
+// A wave's finished item (the whole partition), written from registers:
+// the output row when the sequence has one partition, else its partial.
+template <int DT, int D>
+__device__ __forceinline__ void write_wave_item(const DecodeArgs& a, MfmaState<D>& st,
+                                                const HeadTile& t, int part, int nparts,
+                                                const MfmaLane& ln) {
+  constexpr int EPL = D / 16;
+  float lsum = xor16_combine(st.lsum, AddOp{});
+  lsum = xor32_combine(lsum, AddOp{});
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int hh = 4 * ln.g + e;
+    const float lr = u2f((uint32_t)__builtin_amdgcn_ds_bpermute(hh << 2, (int)f2u(lsum)));
+    const float inv = lr > 0.f ? 1.f / lr : 0.f;
+    if (hh < t.nh) {
+      if (nparts <= 1) {
+#pragma unroll
+        for (int jj = 0; jj < EPL; ++jj)
+          store_elem<DT>(a.out, (t.orow0 + hh) * D + EPL * ln.n + jj, st.o[jj][e] * inv);
+      } else {
+        const int64_t prow = (t.orow0 + hh) * a.max_partitions + part;
+#pragma unroll
+        for (int jj = 0; jj < EPL; ++jj) a.tmp_out[prow * D + EPL * ln.n + jj] = st.o[jj][e] * inv;
+      }
+    }
+  }
+  if (nparts > 1 && ln.g == 0 && ln.n < t.nh) {
+    const int64_t prow = (t.orow0 + ln.n) * a.max_partitions + part;
+    a.max_logits[prow] = st.m * kLn2;
+    a.exp_sums[prow] = lsum;
+  }
+}
+
+// One item: head tile `unit` of sequence s over partition `part` (context
+// L).  WAVE_ITEM: the calling wave alone processes the whole partition and
+// writes its result from registers (no LDS, no barrier); otherwise the NW
+// waves share the partition's blocks and merge through LDS.
+template <int DT, int D, int NW, int DEPTH, bool WAVE_ITEM>
+__device__ __forceinline__ void mfma_item(const DecodeArgs& a, const int unit, const int s,
+                                          const int part, const int L, MfmaLds<D, NW>* sm) {
+  using S = MfmaShape<DT, D>;
+  using VT = typename S::VT;
+  constexpr int EPL = S::EPL;
+  const MfmaLane ln;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+  const HeadTile t = head_tile(a, unit, s);
   const int nblocks = (L + kBlockSize - 1) / kBlockSize;
   const int nparts = (nblocks + a.part_blocks - 1) / a.part_blocks;
-  const int64_t orow0 = (int64_t)s * a.num_q_heads + head0;
   if (L == 0) {
-    for (int i = threadIdx.x; i < nh * D; i += NW * 64) store_elem<DT>(a.out, orow0 * D + i, 0.f);
+    const int t0 = WAVE_ITEM ? (int)(threadIdx.x & 63) : (int)threadIdx.x;
+    const int tn = WAVE_ITEM ? 64 : NW * 64;
+    for (int i = t0; i < t.nh * D; i += tn) store_elem<DT>(a.out, t.orow0 * D + i, 0.f);
     return;
   }
+  u32x4 qb[S::NJ];
+  load_q<DT, D>(a, t, ln, qb);
 
-  // Q^T as the B operand of the S products: column n = head n, slice g of
-  // product j = chunk 4j + g of the head's row.  Idle heads read nothing.
-  u32x4 qb[NJ];
-  {
-    const u32x4* q = reinterpret_cast<const u32x4*>(a.q);
-#pragma unroll
-    for (int jj = 0; jj < NJ; ++jj)
-      qb[jj] = (n < nh) ? q[(orow0 + n) * CPR + 4 * jj + g] : u32x4{0u, 0u, 0u, 0u};
-  }
-
-  constexpr int TILE_BYTES = kBlockSize * D * 2;
-  const char* kbase = static_cast<const char*>(a.k_cache);
-  const char* vbase = static_cast<const char*>(a.v_cache);
   const int32_t* __restrict__ bt = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
   const int jb = part * a.part_blocks;
   const int je = min(jb + a.part_blocks, nblocks);
-  const int j0 = jb + w;                                  // this wave: blocks j0, j0+NW, ...
-  const int nk = je > j0 ? (je - j0 + NW - 1) / NW : 0;  // how many
-  const int tok_k = (n >> 2) + 4 * (n & 3);               // token of S row n
+  constexpr int STRIDE = WAVE_ITEM ? 1 : NW;
+  const int j0 = jb + (WAVE_ITEM ? 0 : w);                         // blocks j0, j0+STRIDE, ...
+  const int nk = je > j0 ? (je - j0 + STRIDE - 1) / STRIDE : 0;  // how many
 
-  float m = -INFINITY;   // running max of head n (base 2)
-  float lsum = 0.f;      // this lane's share of head n's sum (tokens g + 4e)
-  f32x4 o[EPL];
-#pragma unroll
-  for (int jj = 0; jj < EPL; ++jj) o[jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+  MfmaState<D> st;
+  st.reset();
 
   // Pool id of the wave's kk-th block (index clamped into the table row).
-  auto id_at = [&](int kk) -> int { return bt[j0 + min(kk, nk - 1) * NW]; };
+  auto id_at = [&](int kk) -> int { return bt[j0 + min(kk, nk - 1) * STRIDE]; };
   // Descriptors of the wave's kk-th tile and the number of its tokens in the
   // context; empty past the wave's last block or for an id outside the pool.
   auto tile = [&](int kk, int bid, int& limit, Rsrc& rk, Rsrc& rv) {
-    const int j = j0 + min(kk, nk - 1) * NW;
+    const int j = j0 + min(kk, nk - 1) * STRIDE;
     const bool ok = kk < nk && (uint32_t)bid < (uint32_t)a.num_blocks_i32;
     limit = ok ? min(kBlockSize, L - j * kBlockSize) : 0;
-    const int64_t off = ((int64_t)(ok ? bid : 0) * a.num_kv_heads + kvh) * TILE_BYTES;
-    rk = make_rsrc(kbase + off, ok ? TILE_BYTES : 0);
-    rv = make_rsrc(vbase + off, ok ? TILE_BYTES : 0);
-  };
-  auto load = [&](auto shared, Rsrc rk, Rsrc rv, u32x4 (&kr)[NJ], VT (&vr)[4]) {
-    constexpr bool SH = decltype(shared)::value;
-#pragma unroll
-    for (int jj = 0; jj < NJ; ++jj) kr[jj] = buf_load16<SH>(rk, (tok_k * CPR + 4 * jj + g) * 16);
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      vr[e] = VS::template load<SH>(rv, ((g + 4 * e) * 16 + n) * (int)sizeof(VT));
-  };
-  auto consume = [&](auto masked, const u32x4 (&kr)[NJ], VT (&vr)[4], int limit) {
-    constexpr bool MASKED = decltype(masked)::value;
-    f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int jj = 0; jj < NJ; ++jj) sacc = mfma_qk<DT>(kr[jj], qb[jj], sacc);
-    float sc[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      sc[e] = sacc[e] * a.scale_log2;
-      if constexpr (MASKED) {
-        const bool ok = g + 4 * e < limit;
-        sc[e] = ok ? sc[e] : -INFINITY;
-        if (!ok) vr[e] = VT{};  // whatever the slot holds must not reach P.V
-      }
-    }
-    float mb = __builtin_fmaxf(__builtin_fmaxf(sc[0], sc[1]), __builtin_fmaxf(sc[2], sc[3]));
-    mb = xor16_combine(mb, MaxOp{});
-    mb = xor32_combine(mb, MaxOp{});
-    const float mn = __builtin_fmaxf(m, mb);
-    float alpha = fast_exp2(m - mn);
-    float p[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) p[e] = fast_exp2(sc[e] - mn);
-    if constexpr (MASKED) {
-      if (mn == -INFINITY) {  // no valid token of this head so far
-        alpha = 1.f;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) p[e] = 0.f;
-      }
-    }
-    lsum = lsum * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
-    m = mn;
-    // output rows 4g .. 4g+3 are heads 4g+e: fetch their factors
-    float arow[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      arow[e] = u2f((uint32_t)__builtin_amdgcn_ds_bpermute((4 * g + e) << 2, (int)f2u(alpha)));
-    const u32x2 pa{pack2<DT>(p[0], p[1]), pack2<DT>(p[2], p[3])};
-#pragma unroll
-    for (int jj = 0; jj < EPL; ++jj) {
-      const u32x2 vb{VS::half(vr[0], jj) | (VS::half(vr[1], jj) << 16),
-                     VS::half(vr[2], jj) | (VS::half(vr[3], jj) << 16)};
-      f32x4 c = o[jj];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) c[e] *= arow[e];
-      o[jj] = mfma_pv<DT>(pa, vb, c);
-    }
-  };
-  auto consume_block = [&](const u32x4 (&kr)[NJ], VT (&vr)[4], int limit) {
-    if (limit == kBlockSize)
-      consume(std::false_type{}, kr, vr, limit);
-    else
-      consume(std::true_type{}, kr, vr, limit);
+    tile_rsrc<DT, D>(a, bid, t.kvh, ok, rk, rv);
   };
 
   // Software pipeline over the wave's blocks: DEPTH register sets; while
@@ -230,15 +339,16 @@ __device__ __forceinline__ void mfma_item(const DecodeArgs& a, const int hy, con
   // Every step issues its loads (empty past the end) so that the wait counts
   // are the same on every path -- no branch around a load -- and a
   // past-the-end step consumes nothing.
-  u32x4 kr[DEPTH][NJ];
+  u32x4 kr[DEPTH][S::NJ];
   VT vr[DEPTH][4];
   int lim[DEPTH];
   auto pipeline = [&](auto shared) {
+    constexpr bool SH = decltype(shared)::value;
     static_for<0, DEPTH - 1>([&](auto dc) {
       constexpr int d = decltype(dc)::value;
       Rsrc rk, rv;
       tile(d, id_at(d), lim[d], rk, rv);
-      load(shared, rk, rv, kr[d], vr[d]);
+      load_tile<DT, D, SH>(rk, rv, ln, kr[d], vr[d]);
     });
     int next_id = id_at(DEPTH - 1);
     for (int k = 0; k < nk; k += DEPTH) {
@@ -250,8 +360,8 @@ __device__ __forceinline__ void mfma_item(const DecodeArgs& a, const int hy, con
         next_id = id_at(kn + 1);
         Rsrc rk, rv;
         tile(kn, id, lim[dn], rk, rv);
-        load(shared, rk, rv, kr[dn], vr[dn]);
-        consume_block(kr[d], vr[d], lim[d]);
+        load_tile<DT, D, SH>(rk, rv, ln, kr[dn], vr[dn]);
+        consume_any<DT, D>(st, qb, kr[d], vr[d], lim[d], a.scale_log2, ln);
       });
     }
   };
@@ -268,50 +378,55 @@ __device__ __forceinline__ void mfma_item(const DecodeArgs& a, const int hy, con
       pipeline(std::false_type{});
   }
 
+  if constexpr (WAVE_ITEM) {
+    write_wave_item<DT, D>(a, st, t, part, nparts, ln);
+    return;
+  }
   // Per-head totals of this wave, then the cross-wave merge through LDS.
-  lsum = xor16_combine(lsum, AddOp{});
+  const int n = ln.n, g = ln.g;
+  float lsum = xor16_combine(st.lsum, AddOp{});
   lsum = xor32_combine(lsum, AddOp{});
   if (g == 0) {
-    sm.m[w][n] = m;
-    sm.l[w][n] = lsum;
+    sm->m[w][n] = st.m;
+    sm->l[w][n] = lsum;
   }
 #pragma unroll
   for (int e = 0; e < 4; ++e)
 #pragma unroll
-    for (int jj = 0; jj < EPL; ++jj) sm.o[w][4 * g + e][EPL * n + jj] = o[jj][e];
+    for (int jj = 0; jj < EPL; ++jj) sm->o[w][4 * g + e][EPL * n + jj] = st.o[jj][e];
   __syncthreads();
   if (threadIdx.x < 16) {
     const int hh = threadIdx.x;
     float M = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < NW; ++i) M = __builtin_fmaxf(M, sm.m[i][hh]);
+    for (int i = 0; i < NW; ++i) M = __builtin_fmaxf(M, sm->m[i][hh]);
     float tot = 0.f;
     float f[NW];
 #pragma unroll
     for (int i = 0; i < NW; ++i) {
-      f[i] = (sm.m[i][hh] == -INFINITY) ? 0.f : fast_exp2(sm.m[i][hh] - M);
-      tot += sm.l[i][hh] * f[i];
+      f[i] = (sm->m[i][hh] == -INFINITY) ? 0.f : fast_exp2(sm->m[i][hh] - M);
+      tot += sm->l[i][hh] * f[i];
     }
     const float inv = tot > 0.f ? 1.f / tot : 0.f;
 #pragma unroll
-    for (int i = 0; i < NW; ++i) sm.f[i][hh] = f[i] * inv;
-    sm.tot[hh] = tot;
-    sm.mx[hh] = M;
+    for (int i = 0; i < NW; ++i) sm->f[i][hh] = f[i] * inv;
+    sm->tot[hh] = tot;
+    sm->mx[hh] = M;
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < nh * D; i += NW * 64) {
+  for (int i = threadIdx.x; i < t.nh * D; i += NW * 64) {
     const int hh = i / D, d = i % D;
     float v = 0.f;
 #pragma unroll
-    for (int k = 0; k < NW; ++k) v += sm.o[k][hh][d] * sm.f[k][hh];
+    for (int k = 0; k < NW; ++k) v += sm->o[k][hh][d] * sm->f[k][hh];
     if (nparts <= 1) {
-      store_elem<DT>(a.out, (orow0 + hh) * D + d, v);
+      store_elem<DT>(a.out, (t.orow0 + hh) * D + d, v);
     } else {
-      const int64_t prow = (orow0 + hh) * a.max_partitions + part;
+      const int64_t prow = (t.orow0 + hh) * a.max_partitions + part;
       a.tmp_out[prow * D + d] = v;
       if (d == 0) {
-        a.max_logits[prow] = sm.mx[hh] * kLn2;
-        a.exp_sums[prow] = sm.tot[hh];
+        a.max_logits[prow] = sm->mx[hh] * kLn2;
+        a.exp_sums[prow] = sm->tot[hh];
       }
     }
   }
@@ -327,8 +442,162 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
   const int unit = blockIdx.x, s = blockIdx.y, part = blockIdx.z;
   const int L = clamp_len(a, s);
   if (part >= parts_of(L, a.part_blocks)) return;  // past this sequence's end
-  mfma_item<DT, D, NW, DEPTH>(a, unit, s, part, L, sm);
+  mfma_item<DT, D, NW, DEPTH, false>(a, unit, s, part, L, &sm);
 }
+
+// One wave per item: wave w of workgroup z takes partition z * NW + w, for
+// launches with many partitions per sequence.
+template <int DT, int D, int NW, int DEPTH>
+__global__ __launch_bounds__(NW * 64) void decode_mfma_wave_kernel(DecodeArgs a) {
+  const int unit = blockIdx.x, s = blockIdx.y;
+  const int part = blockIdx.z * NW + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int L = clamp_len(a, s);
+  if (part >= parts_of(L, a.part_blocks)) return;  // past this sequence's end
+  mfma_item<DT, D, NW, DEPTH, true>(a, unit, s, part, L, nullptr);
+}
+
+// Position in the compact item list (sequence-major, then head unit, then
+// partition) and in the blocks of the current item.
+struct StreamCursor {
+  int s, unit, part, nparts, len, nblocks;
+  int j, jend;     // current block, end of the item's blocks (>= j + 1)
+  int64_t item;    // index in the compact list
+  __device__ __forceinline__ void enter_item(const DecodeArgs& a) {
+    j = part * a.part_blocks;
+    jend = max(j + 1, min(j + a.part_blocks, nblocks));  // an empty context still takes a step
+  }
+  __device__ __forceinline__ void enter_seq(const DecodeArgs& a) {
+    len = clamp_len(a, s);
+    nblocks = (len + kBlockSize - 1) / kBlockSize;
+    nparts = parts_of(len, a.part_blocks);
+  }
+  // Place the cursor on item `idx` (walks the sequences).
+  __device__ __forceinline__ void seek(const DecodeArgs& a, int units, int64_t idx) {
+    int64_t cum = 0;
+    for (s = 0; s < a.num_seqs - 1; ++s) {
+      const int64_t n = (int64_t)units * parts_of(clamp_len(a, s), a.part_blocks);
+      if (idx < cum + n) break;
+      cum += n;
+    }
+    enter_seq(a);
+    const int r = (int)(idx - cum);
+    unit = r / nparts;
+    part = r % nparts;
+    item = idx;
+    enter_item(a);
+  }
+  __device__ __forceinline__ bool last_block() const { return j + 1 >= jend; }
+  // Step to the next block (and item, head unit, sequence as they end).
+  __device__ __forceinline__ void advance(const DecodeArgs& a, int units) {
+    if (++j < jend) return;
+    ++item;
+    if (++part == nparts) {
+      part = 0;
+      if (++unit == units) {
+        unit = 0;
+        if (s + 1 < a.num_seqs) ++s;
+        enter_seq(a);
+      }
+    }
+    enter_item(a);
+  }
+};
+
+// Streaming mode, for launches with many partitions and few sequences: every
+// resident wave is a worker that takes an equal contiguous share of the
+// compact item list and streams the blocks of all its items through one
+// load pipeline, writing each item's partial (or output row) as soon as its
+// last block is consumed.  No workgroup is ever empty, no item pays a
+// pipeline start-up, and the partitions stay exactly the ones the reduce
+// merges.
+template <int DT, int D, int NW, int DEPTH>
+__global__ __launch_bounds__(NW * 64) void decode_mfma_stream_kernel(DecodeArgs a) {
+  using S = MfmaShape<DT, D>;
+  using VT = typename S::VT;
+  const MfmaLane ln;
+  const int group = a.num_q_heads / a.num_kv_heads;
+  const int units = a.num_kv_heads * ((group + 15) >> 4);
+
+  int64_t total = 0;
+  for (int s = 0; s < a.num_seqs; ++s)
+    total += (int64_t)units * parts_of(clamp_len(a, s), a.part_blocks);
+  const int64_t workers = (int64_t)gridDim.x * NW;
+  const int64_t wid = (int64_t)blockIdx.x * NW + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t i0 = total * wid / workers, i1 = total * (wid + 1) / workers;
+  if (i0 >= i1) return;
+
+  StreamCursor lc, cc;  // load cursor (runs DEPTH-1 steps ahead), consume cursor
+  lc.seek(a, units, i0);
+  cc = lc;
+  HeadTile t = head_tile(a, cc.unit, cc.s);
+  u32x4 qb[S::NJ];
+  load_q<DT, D>(a, t, ln, qb);
+  int q_s = cc.s, q_unit = cc.unit;
+  MfmaState<D> st;
+  st.reset();
+
+  u32x4 kr[DEPTH][S::NJ];
+  VT vr[DEPTH][4];
+  int lim[DEPTH];
+  // Issue the loads of the load cursor's block (empty once past this
+  // worker's range) and step the cursor.
+  auto issue = [&](int slot, int bid) {
+    const bool live = lc.item < i1;
+    const HeadTile lt = head_tile(a, lc.unit, lc.s);
+    Rsrc rk, rv;
+    tile_rsrc<DT, D>(a, bid, lt.kvh, live && lc.j < lc.nblocks, rk, rv);
+    lim[slot] = (live && (uint32_t)bid < (uint32_t)a.num_blocks_i32)
+                    ? max(0, min(kBlockSize, lc.len - lc.j * kBlockSize))
+                    : 0;
+    load_tile<DT, D, false>(rk, rv, ln, kr[slot], vr[slot]);
+    if (live) lc.advance(a, units);
+  };
+  auto id_of = [&](const StreamCursor& c) -> int {
+    return (c.item < i1 && c.j < c.nblocks)
+               ? a.block_tables[(int64_t)c.s * a.max_blocks_per_seq + c.j]
+               : 0;
+  };
+
+  static_for<0, DEPTH - 1>([&](auto dc) { issue(decltype(dc)::value, id_of(lc)); });
+  int next_id = id_of(lc);
+  bool running = true;
+  while (running) {
+    static_for<0, DEPTH>([&](auto dc) {
+      constexpr int d = decltype(dc)::value;
+      constexpr int dn = (d + DEPTH - 1) % DEPTH;
+      const int id = next_id;
+      issue(dn, id);
+      next_id = id_of(lc);
+      if (running) {
+        if (cc.s != q_s || cc.unit != q_unit) {  // a new head tile: its query
+          t = head_tile(a, cc.unit, cc.s);
+          load_q<DT, D>(a, t, ln, qb);
+          q_s = cc.s;
+          q_unit = cc.unit;
+        }
+        consume_any<DT, D>(st, qb, kr[d], vr[d], lim[d], a.scale_log2, ln);
+        if (cc.last_block()) {
+          if (cc.len == 0) {  // empty context: zero row
+            for (int i = threadIdx.x & 63; i < t.nh * D; i += 64)
+              store_elem<DT>(a.out, t.orow0 * D + i, 0.f);
+          } else {
+            write_wave_item<DT, D>(a, st, t, cc.part, cc.nparts, ln);
+          }
+          st.reset();
+          running = cc.item + 1 < i1;
+        }
+        cc.advance(a, units);
+      }
+    });
+  }
+}
+
+#ifndef PA_MFMA_WAVE_ITEM_WAVES
+#define PA_MFMA_WAVE_ITEM_WAVES 4  // waves (= partitions) per workgroup, one-wave items
+#endif
+#ifndef PA_MFMA_WAVE_ITEM_DEPTH
+#define PA_MFMA_WAVE_ITEM_DEPTH 3  // tiles per wave in the load pipeline, one-wave items
+#endif
 
 // Launch shapes: items of at least kLongItemBlocks blocks get 8 waves,
 // shorter ones 4 (more workgroups resident per CU).
@@ -342,8 +611,51 @@ hipError_t launch_shape(const DecodeArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Launches with at least kWaveItemParts partitions take one wave per item;
+// with at most kStreamMaxSeqs sequences as well, the streaming mode.
+constexpr int kWaveItemParts = 8;
+#ifndef PA_STREAM_MAX_SEQS
+#define PA_STREAM_MAX_SEQS 64
+#endif
+#ifndef PA_MFMA_STREAM_WAVES
+#define PA_MFMA_STREAM_WAVES 4  // waves per workgroup, streaming mode
+#endif
+#ifndef PA_MFMA_STREAM_DEPTH
+#define PA_MFMA_STREAM_DEPTH 3  // tiles per wave in the load pipeline, streaming mode
+#endif
+constexpr int kStreamMaxSeqs = PA_STREAM_MAX_SEQS;
+
+template <int DT, int D, int NW, int DEPTH>
+hipError_t launch_wave_shape(const DecodeArgs& a, hipStream_t stream) {
+  const int group = a.num_q_heads / a.num_kv_heads;
+  const dim3 grid(a.num_kv_heads * ((group + 15) / 16), a.num_seqs,
+                  (a.max_partitions + NW - 1) / NW);
+  hipLaunchKernelGGL((decode_mfma_wave_kernel<DT, D, NW, DEPTH>), grid, dim3(NW * 64), 0, stream,
+                     a);
+  return hipGetLastError();
+}
+
+template <int DT, int D, int NW, int DEPTH>
+hipError_t launch_stream_shape(const DecodeArgs& a, hipStream_t stream) {
+  const auto kernel = decode_mfma_stream_kernel<DT, D, NW, DEPTH>;
+  static ResidentCache cache;
+  const int group = a.num_q_heads / a.num_kv_heads;
+  const int64_t items = (int64_t)a.num_kv_heads * ((group + 15) / 16) * a.num_seqs *
+                        a.max_partitions;
+  const int grid = resident_workgroups(reinterpret_cast<const void*>(kernel), NW * 64, cache);
+  if (grid <= 0) return hipErrorInvalidValue;
+  const int64_t need = (items + NW - 1) / NW;  // never more workers than items
+  hipLaunchKernelGGL(kernel, dim3((unsigned)(need < grid ? need : grid)), dim3(NW * 64), 0,
+                     stream, a);
+  return hipGetLastError();
+}
+
 template <int DT, int D>
 hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
+  if (a.max_partitions >= kWaveItemParts && a.num_seqs <= kStreamMaxSeqs)
+    return launch_stream_shape<DT, D, PA_MFMA_STREAM_WAVES, PA_MFMA_STREAM_DEPTH>(a, stream);
+  if (a.max_partitions >= kWaveItemParts)
+    return launch_wave_shape<DT, D, PA_MFMA_WAVE_ITEM_WAVES, PA_MFMA_WAVE_ITEM_DEPTH>(a, stream);
   return a.part_blocks >= kLongItemBlocks ? launch_shape<DT, D, 8, 2>(a, stream)
                                           : launch_shape<DT, D, 4, 2>(a, stream);
 }

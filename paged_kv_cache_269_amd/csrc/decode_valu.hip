@@ -55,9 +55,12 @@ struct ValuLds {
 };
 
 // One item: query head h of sequence s over partition `part` (context L).
-template <int DT, int D, int NW, int DEPTH>
+// WAVE_ITEM: the calling wave alone processes the whole partition and merges
+// its rows in registers (no LDS, no barrier); otherwise the NW waves of the
+// workgroup share the partition's blocks and merge through LDS.
+template <int DT, int D, int NW, int DEPTH, bool WAVE_ITEM>
 __device__ __forceinline__ void valu_item(const DecodeArgs& a, const int h, const int s,
-                                          const int part, const int L, ValuLds<DT, D, NW>& sm) {
+                                          const int part, const int L, ValuLds<DT, D, NW>* sm) {
   using S = ValuShape<DT, D>;
   constexpr int VEC = S::VEC, LPT = S::LPT, TPL = S::TPL, NLD = S::NLD;
 
@@ -70,7 +73,8 @@ __device__ __forceinline__ void valu_item(const DecodeArgs& a, const int h, cons
   const int nparts = (nblocks + a.part_blocks - 1) / a.part_blocks;
   const int64_t orow = (int64_t)s * a.num_q_heads + h;
   if (L == 0) {
-    for (int d = threadIdx.x; d < D; d += NW * 64) store_elem<DT>(a.out, orow * D + d, 0.f);
+    const int t0 = WAVE_ITEM ? lane : (int)threadIdx.x, tn = WAVE_ITEM ? 64 : NW * 64;
+    for (int d = t0; d < D; d += tn) store_elem<DT>(a.out, orow * D + d, 0.f);
     return;
   }
 
@@ -80,8 +84,9 @@ __device__ __forceinline__ void valu_item(const DecodeArgs& a, const int h, cons
   const int32_t* __restrict__ bt = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
   const int jb = part * a.part_blocks;
   const int je = min(jb + a.part_blocks, nblocks);
-  const int j0 = jb + w;                                  // this wave: blocks j0, j0+NW, ...
-  const int nk = je > j0 ? (je - j0 + NW - 1) / NW : 0;  // how many
+  constexpr int STRIDE = WAVE_ITEM ? 1 : NW;
+  const int j0 = jb + (WAVE_ITEM ? 0 : w);                         // blocks j0, j0+STRIDE, ...
+  const int nk = je > j0 ? (je - j0 + STRIDE - 1) / STRIDE : 0;  // how many
 
   float m = -INFINITY, l = 0.f;
   float acc[VEC];
@@ -89,12 +94,12 @@ __device__ __forceinline__ void valu_item(const DecodeArgs& a, const int h, cons
   for (int k = 0; k < VEC; ++k) acc[k] = 0.f;
 
   // Pool id of the wave's kk-th block (index clamped into the table row).
-  auto id_at = [&](int kk) -> int { return bt[j0 + min(kk, nk - 1) * NW]; };
+  auto id_at = [&](int kk) -> int { return bt[j0 + min(kk, nk - 1) * STRIDE]; };
   // Descriptors of the wave's kk-th tile and the number of its tokens in the
   // context; past the wave's last block, or for an id outside the pool, the
   // descriptors are empty and no token counts.
   auto tile = [&](int kk, int bid, int& limit, Rsrc& rk, Rsrc& rv) {
-    const int j = j0 + min(kk, nk - 1) * NW;
+    const int j = j0 + min(kk, nk - 1) * STRIDE;
     const bool ok = kk < nk && (uint32_t)bid < (uint32_t)a.num_blocks_i32;
     limit = ok ? min(kBlockSize, L - j * kBlockSize) : 0;
     const int64_t off = ((int64_t)(ok ? bid : 0) * a.num_kv_heads + kvh) * S::TILE_BYTES;
@@ -190,27 +195,53 @@ __device__ __forceinline__ void valu_item(const DecodeArgs& a, const int h, cons
       pipeline(std::false_type{});
   }
 
+  if constexpr (WAVE_ITEM) {
+    // Merge this wave's TPL row states in registers; row 0 writes.
+    const float M = across_groups<LPT>(m, MaxOp{});
+    const float f = (m == -INFINITY) ? 0.f : fast_exp2(m - M);
+    const float lsum = across_groups<LPT>(l * f, AddOp{});
+    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+    float o[VEC];
+#pragma unroll
+    for (int k = 0; k < VEC; ++k) o[k] = across_groups<LPT>(acc[k] * f, AddOp{}) * inv;
+    if (row == 0) {
+      if (nparts <= 1) {
+        store16<DT>(a.out, orow * D + c * VEC, o);
+      } else {
+        const int64_t prow = orow * a.max_partitions + part;
+#pragma unroll
+        for (int k = 0; k < VEC; k += 4)  // fp32 partials: 16 bytes = 4 values per store
+          store16<kF32>(a.tmp_out, prow * D + c * VEC + k, o + k);
+        if (c == 0) {
+          a.max_logits[prow] = M * kLn2;  // back to natural-log units
+          a.exp_sums[prow] = lsum;
+        }
+      }
+    }
+    return;
+  }
+
   // Merge the TPL x NW partial states of this partition.
   constexpr int R = NW * TPL;
   const int r = w * TPL + row;
   if (c == 0) {
-    sm.m[r] = m;
-    sm.l[r] = l;
+    sm->m[r] = m;
+    sm->l[r] = l;
   }
 #pragma unroll
-  for (int k = 0; k < VEC; ++k) sm.acc[r * D + c * VEC + k] = acc[k];
+  for (int k = 0; k < VEC; ++k) sm->acc[r * D + c * VEC + k] = acc[k];
   __syncthreads();
 
   for (int d = threadIdx.x; d < D; d += NW * 64) {
     float M = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < R; ++i) M = __builtin_fmaxf(M, sm.m[i]);
+    for (int i = 0; i < R; ++i) M = __builtin_fmaxf(M, sm->m[i]);
     float lsum = 0.f, o = 0.f;
 #pragma unroll
     for (int i = 0; i < R; ++i) {
-      const float f = (sm.m[i] == -INFINITY) ? 0.f : fast_exp2(sm.m[i] - M);
-      lsum += sm.l[i] * f;
-      o += sm.acc[i * D + d] * f;
+      const float f = (sm->m[i] == -INFINITY) ? 0.f : fast_exp2(sm->m[i] - M);
+      lsum += sm->l[i] * f;
+      o += sm->acc[i * D + d] * f;
     }
     o = lsum > 0.f ? o / lsum : 0.f;
     if (nparts <= 1) {
@@ -236,8 +267,27 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(DecodeArgs a) {
   const int unit = blockIdx.x, s = blockIdx.y, part = blockIdx.z;
   const int L = clamp_len(a, s);
   if (part >= parts_of(L, a.part_blocks)) return;  // past this sequence's end
-  valu_item<DT, D, NW, DEPTH>(a, unit, s, part, L, sm);
+  valu_item<DT, D, NW, DEPTH, false>(a, unit, s, part, L, &sm);
 }
+
+// One wave per item: wave w of workgroup z takes partition z * NW + w, for
+// launches with many partitions per sequence (each wave then streams a whole
+// partition; there is no cross-wave merge).
+template <int DT, int D, int NW, int DEPTH>
+__global__ __launch_bounds__(NW * 64) void decode_valu_wave_kernel(DecodeArgs a) {
+  const int unit = blockIdx.x, s = blockIdx.y;
+  const int part = blockIdx.z * NW + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int L = clamp_len(a, s);
+  if (part >= parts_of(L, a.part_blocks)) return;  // past this sequence's end
+  valu_item<DT, D, NW, DEPTH, true>(a, unit, s, part, L, nullptr);
+}
+
+#ifndef PA_WAVE_ITEM_WAVES
+#define PA_WAVE_ITEM_WAVES 4  // waves (= partitions) per workgroup, one-wave items
+#endif
+#ifndef PA_WAVE_ITEM_DEPTH
+#define PA_WAVE_ITEM_DEPTH 3  // tiles per wave in the load pipeline, one-wave items
+#endif
 
 // Launch shapes: items of at least kLongItemBlocks blocks get 8 waves and a
 // 3-deep load pipeline (more bytes in flight per item); shorter items get 4
@@ -251,8 +301,20 @@ hipError_t launch_shape(const DecodeArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Launches with at least kWaveItemParts partitions take one wave per item.
+constexpr int kWaveItemParts = 8;
+
+template <int DT, int D, int NW, int DEPTH>
+hipError_t launch_wave_shape(const DecodeArgs& a, hipStream_t stream) {
+  const dim3 grid(a.num_q_heads, a.num_seqs, (a.max_partitions + NW - 1) / NW);
+  hipLaunchKernelGGL((decode_valu_wave_kernel<DT, D, NW, DEPTH>), grid, dim3(NW * 64), 0, stream,
+                     a);
+  return hipGetLastError();
+}
+
 template <int DT, int D>
 hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
+  if (a.max_partitions >= kWaveItemParts) return launch_wave_shape<DT, D, PA_WAVE_ITEM_WAVES, PA_WAVE_ITEM_DEPTH>(a, stream);
   return a.part_blocks >= kLongItemBlocks ? launch_shape<DT, D, 8, 3>(a, stream)
                                           : launch_shape<DT, D, 4, 2>(a, stream);
 }

@@ -20,4 +20,26 @@ __device__ __forceinline__ int parts_of(int L, int part_blocks) {
   return P > 0 ? P : 1;
 }
 
+// Host: workgroups of `kernel` (block of `threads`) resident on the current
+// device at once, cached per device.  Returns <= 0 on a runtime error.
+struct ResidentCache {
+  int per_device[64] = {};
+};
+
+inline int resident_workgroups(const void* kernel, int threads, ResidentCache& c) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  const bool cacheable = dev >= 0 && dev < 64;
+  int resident = cacheable ? __atomic_load_n(&c.per_device[dev], __ATOMIC_RELAXED) : 0;
+  if (resident <= 0) {
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return -1;
+    resident = per_cu * cus;
+    if (cacheable && resident > 0) __atomic_store_n(&c.per_device[dev], resident, __ATOMIC_RELAXED);
+  }
+  return resident;
+}
+
 }  // namespace pa

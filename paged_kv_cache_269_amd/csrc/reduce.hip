@@ -8,10 +8,11 @@
 // partitions processed in parallel; it runs after the decode kernel on the
 // same stream.
 //
-// One workgroup (256 lanes) per (query head, sequence): the weights of up to
-// 256 partitions at a time go to LDS, then 256 / head_dim lane groups each
+// One workgroup (512 lanes) per (query head, sequence): the weights of up to
+// 512 partitions at a time go to LDS, then 512 / head_dim lane groups each
 // sweep a share of those partitions over all head_dim columns (coalesced
-// reads of tmp_out rows), and the shares are added at the end.
+// reads of tmp_out rows, kUnroll independent loads in flight per lane), and
+// the shares are added at the end.
 #include "common.h"
 #include "launch.h"
 
@@ -19,7 +20,8 @@ namespace pa {
 
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
+constexpr int kUnroll = 8;
 
 __device__ __forceinline__ float block_max(float x, float* scratch) {
   x = group_reduce<64>(x, MaxOp{});
@@ -69,10 +71,21 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(ReduceArgs a) {
     s_w[tid] = wv;
     __syncthreads();
     const int cnt = min(kThreads, P - p0);
-    for (int k = share; k < cnt; k += SPLIT) {
-      const float ww = s_w[k];
-      wsum += ww;
-      if (ww != 0.f) o += ww * a.tmp_out[(base + p0 + k) * D + d];
+    for (int k = share; k < cnt; k += SPLIT * kUnroll) {
+      float t[kUnroll], wv[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {  // loads issued unconditionally (index kept in range)
+        const int kk = k + u * SPLIT;
+        const bool in = kk < cnt;
+        const int ki = in ? kk : share;
+        wv[u] = in ? s_w[ki] : 0.f;
+        t[u] = a.tmp_out[(base + p0 + ki) * D + d];
+      }
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        wsum += wv[u];
+        o += wv[u] != 0.f ? wv[u] * t[u] : 0.f;  // a weightless row may hold anything
+      }
     }
     __syncthreads();
   }
