@@ -1,6 +1,6 @@
 // C-ABI host layer of libpagedattn: argument checks, kernel choice, launches.
 // Declarations and the meaning of every argument: include/pagedattn.h.
-#include "../../include/pagedattn.h"
+#include "pagedattn.h"
 
 #include <hip/hip_runtime.h>
 

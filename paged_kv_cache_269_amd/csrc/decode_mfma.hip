@@ -174,29 +174,68 @@ __device__ __forceinline__ void tile_rsrc(const DecodeArgs& a, int bid, int kvh,
   rv = make_rsrc(static_cast<const char*>(a.v_cache) + off, ok ? S::TILE_BYTES : 0);
 }
 
-// The lane's share of one tile: K rows tau(n) (A operand of S), V rows g+4e.
+// The lane's share of one tile.  K: load jj is the tile's jj-th contiguous
+// KiB (lane l takes its 16-byte chunk l), so every load reads whole cache
+// lines; the rows reach the matrix-core layout through LDS (stage_k).  V:
+// rows g + 4e, already in the P.V operand layout.
 template <int DT, int D, bool SH>
 __device__ __forceinline__ void load_tile(Rsrc rk, Rsrc rv, const MfmaLane& ln,
                                           u32x4 (&kr)[D / 32],
                                           typename MfmaShape<DT, D>::VT (&vr)[4]) {
   using S = MfmaShape<DT, D>;
+  const int lane = ln.n + 16 * ln.g;
 #pragma unroll
-  for (int jj = 0; jj < S::NJ; ++jj)
-    kr[jj] = buf_load16<SH>(rk, (ln.tok_k * S::CPR + 4 * jj + ln.g) * 16);
+  for (int jj = 0; jj < S::NJ; ++jj) kr[jj] = buf_load16<SH>(rk, (jj * 64 + lane) * 16);
 #pragma unroll
   for (int e = 0; e < 4; ++e)
     vr[e] = S::VS::template load<SH>(rv, ((ln.g + 4 * e) * 16 + ln.n) *
                                              (int)sizeof(typename S::VT));
 }
 
+// Force the wait for registers just loaded (an empty asm reading them).
+template <int N>
+__device__ __forceinline__ void wait_loaded(const u32x4 (&x)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) asm volatile("" ::"v"(x[i]));
+}
+
+// 16-byte slot of K chunk c of token row r in a wave's LDS staging tile.
+// Rows are padded by one chunk: both the row-wise writes and the
+// column-wise reads of the S operand then spread over the LDS banks, and
+// every load/store of one lane differs from its others by a constant offset.
+template <int D>
+__device__ __forceinline__ int kslot(int r, int c) {
+  return r * (D / 8 + 1) + c;
+}
+template <int D>
+constexpr int kKStageSlots = kBlockSize * (D / 8 + 1);
+
+// K tile (as loaded: load jj, lane l = chunk jj*64 + l of the tile) through
+// the wave's own LDS tile into the S operand layout, in place: lane (n, g) of
+// product jj gets chunk 4jj + g of token row tau(n).  Only this wave touches
+// `kst`, and its LDS accesses complete in order, so no barrier is needed.
+template <int D>
+__device__ __forceinline__ void stage_k(u32x4* kst, u32x4 (&kr)[D / 32], const MfmaLane& ln) {
+  constexpr int CPR = D / 8, NJ = D / 32;
+  const int lane = ln.n + 16 * ln.g;
+#pragma unroll
+  for (int jj = 0; jj < NJ; ++jj) {
+    const int idx = jj * 64 + lane;
+    kst[kslot<D>(idx / CPR, idx % CPR)] = kr[jj];
+  }
+#pragma unroll
+  for (int jj = 0; jj < NJ; ++jj) kr[jj] = kst[kslot<D>(ln.tok_k, 4 * jj + ln.g)];
+}
+
 // Fold one tile (`limit` of its 16 tokens in the context) into the state.
 template <int DT, int D, bool MASKED>
 __device__ __forceinline__ void consume_tile(MfmaState<D>& st, const u32x4 (&qb)[D / 32],
-                                             const u32x4 (&kr)[D / 32],
+                                             u32x4 (&kr)[D / 32],
                                              typename MfmaShape<DT, D>::VT (&vr)[4], int limit,
-                                             float scale_log2, const MfmaLane& ln) {
+                                             float scale_log2, const MfmaLane& ln, u32x4* kst) {
   using S = MfmaShape<DT, D>;
   using VT = typename S::VT;
+  stage_k<D>(kst, kr, ln);
   f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int jj = 0; jj < S::NJ; ++jj) sacc = mfma_qk<DT>(kr[jj], qb[jj], sacc);
@@ -213,46 +252,53 @@ __device__ __forceinline__ void consume_tile(MfmaState<D>& st, const u32x4 (&qb)
   float mb = __builtin_fmaxf(__builtin_fmaxf(sc[0], sc[1]), __builtin_fmaxf(sc[2], sc[3]));
   mb = xor16_combine(mb, MaxOp{});
   mb = xor32_combine(mb, MaxOp{});
-  const float mn = __builtin_fmaxf(st.m, mb);
-  float alpha = fast_exp2(st.m - mn);
+  // The running max moves only when a score passes it by more than
+  // kRescaleSlack: until then the tile's weights are taken against the older
+  // max (each below 2^kRescaleSlack) and the accumulators keep their scale.
+  // Numerator and denominator share that max, so the result is unchanged.
+  if (__builtin_amdgcn_ballot_w64(mb > st.m + kRescaleSlack) != 0) {  // wave-uniform
+    const float mn = __builtin_fmaxf(st.m, mb);
+    const float alpha = mn == -INFINITY ? 1.f : fast_exp2(st.m - mn);
+    st.lsum *= alpha;
+    st.m = mn;
+    // output rows 4g .. 4g+3 are heads 4g+e: fetch their factors
+    float arow[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      arow[e] = u2f((uint32_t)__builtin_amdgcn_ds_bpermute((4 * ln.g + e) << 2, (int)f2u(alpha)));
+#pragma unroll
+    for (int jj = 0; jj < S::EPL; ++jj)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) st.o[jj][e] *= arow[e];
+  }
   float p[4];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) p[e] = fast_exp2(sc[e] - mn);
+  for (int e = 0; e < 4; ++e) p[e] = fast_exp2(sc[e] - st.m);
   if constexpr (MASKED) {
-    if (mn == -INFINITY) {  // no valid token of this head so far
-      alpha = 1.f;
+    if (st.m == -INFINITY) {  // no valid token of this head so far
 #pragma unroll
       for (int e = 0; e < 4; ++e) p[e] = 0.f;
     }
   }
-  st.lsum = st.lsum * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
-  st.m = mn;
-  // output rows 4g .. 4g+3 are heads 4g+e: fetch their factors
-  float arow[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e)
-    arow[e] = u2f((uint32_t)__builtin_amdgcn_ds_bpermute((4 * ln.g + e) << 2, (int)f2u(alpha)));
+  st.lsum += (p[0] + p[1]) + (p[2] + p[3]);
   const u32x2 pa{pack2<DT>(p[0], p[1]), pack2<DT>(p[2], p[3])};
 #pragma unroll
   for (int jj = 0; jj < S::EPL; ++jj) {
     const u32x2 vb{S::VS::half(vr[0], jj) | (S::VS::half(vr[1], jj) << 16),
                    S::VS::half(vr[2], jj) | (S::VS::half(vr[3], jj) << 16)};
-    f32x4 c = st.o[jj];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) c[e] *= arow[e];
-    st.o[jj] = mfma_pv<DT>(pa, vb, c);
+    st.o[jj] = mfma_pv<DT>(pa, vb, st.o[jj]);
   }
 }
 
 template <int DT, int D>
 __device__ __forceinline__ void consume_any(MfmaState<D>& st, const u32x4 (&qb)[D / 32],
-                                            const u32x4 (&kr)[D / 32],
+                                            u32x4 (&kr)[D / 32],
                                             typename MfmaShape<DT, D>::VT (&vr)[4], int limit,
-                                            float scale_log2, const MfmaLane& ln) {
+                                            float scale_log2, const MfmaLane& ln, u32x4* kst) {
   if (limit == kBlockSize)
-    consume_tile<DT, D, false>(st, qb, kr, vr, limit, scale_log2, ln);
+    consume_tile<DT, D, false>(st, qb, kr, vr, limit, scale_log2, ln, kst);
   else
-    consume_tile<DT, D, true>(st, qb, kr, vr, limit, scale_log2, ln);
+    consume_tile<DT, D, true>(st, qb, kr, vr, limit, scale_log2, ln, kst);
 }
 
 // A wave's finished item (the whole partition), written from registers:
@@ -288,13 +334,24 @@ __device__ __forceinline__ void write_wave_item(const DecodeArgs& a, MfmaState<D
   }
 }
 
+// Partitions p0 .. p1 of a head tile hold no result of their own (their
+// tokens were folded into an earlier slot): weight zero for the reduce.
+__device__ __forceinline__ void mark_empty(const DecodeArgs& a, const HeadTile& t, int p0, int p1,
+                                           const MfmaLane& ln) {
+  if (ln.n >= t.nh) return;
+  const int64_t row = (t.orow0 + ln.n) * a.max_partitions;
+  for (int p = p0 + ln.g; p <= p1; p += 4) a.exp_sums[row + p] = 0.f;
+}
+
 // One item: head tile `unit` of sequence s over partition `part` (context
 // L).  WAVE_ITEM: the calling wave alone processes the whole partition and
-// writes its result from registers (no LDS, no barrier); otherwise the NW
-// waves share the partition's blocks and merge through LDS.
+// writes its result from registers (no merge, no barrier); otherwise the NW
+// waves share the partition's blocks and merge through LDS.  `kst` is the
+// calling wave's K staging tile.
 template <int DT, int D, int NW, int DEPTH, bool WAVE_ITEM>
 __device__ __forceinline__ void mfma_item(const DecodeArgs& a, const int unit, const int s,
-                                          const int part, const int L, MfmaLds<D, NW>* sm) {
+                                          const int part, const int L, MfmaLds<D, NW>* sm,
+                                          u32x4* kst) {
   using S = MfmaShape<DT, D>;
   using VT = typename S::VT;
   constexpr int EPL = S::EPL;
@@ -361,7 +418,7 @@ __device__ __forceinline__ void mfma_item(const DecodeArgs& a, const int unit, c
         Rsrc rk, rv;
         tile(kn, id, lim[dn], rk, rv);
         load_tile<DT, D, SH>(rk, rv, ln, kr[dn], vr[dn]);
-        consume_any<DT, D>(st, qb, kr[d], vr[d], lim[d], a.scale_log2, ln);
+        consume_any<DT, D>(st, qb, kr[d], vr[d], lim[d], a.scale_log2, ln, kst);
       });
     }
   };
@@ -439,69 +496,86 @@ __device__ __forceinline__ void mfma_item(const DecodeArgs& a, const int unit, c
 template <int DT, int D, int NW, int DEPTH>
 __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
   __shared__ MfmaLds<D, NW> sm;
+  __shared__ u32x4 kst[NW][kKStageSlots<D>];
   const int unit = blockIdx.x, s = blockIdx.y, part = blockIdx.z;
   const int L = clamp_len(a, s);
   if (part >= parts_of(L, a.part_blocks)) return;  // past this sequence's end
-  mfma_item<DT, D, NW, DEPTH, false>(a, unit, s, part, L, &sm);
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  mfma_item<DT, D, NW, DEPTH, false>(a, unit, s, part, L, &sm, kst[w]);
 }
 
 // One wave per item: wave w of workgroup z takes partition z * NW + w, for
 // launches with many partitions per sequence.
 template <int DT, int D, int NW, int DEPTH>
 __global__ __launch_bounds__(NW * 64) void decode_mfma_wave_kernel(DecodeArgs a) {
+  __shared__ u32x4 kst[NW][kKStageSlots<D>];
   const int unit = blockIdx.x, s = blockIdx.y;
-  const int part = blockIdx.z * NW + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int part = blockIdx.z * NW + w;
   const int L = clamp_len(a, s);
   if (part >= parts_of(L, a.part_blocks)) return;  // past this sequence's end
-  mfma_item<DT, D, NW, DEPTH, true>(a, unit, s, part, L, nullptr);
+  mfma_item<DT, D, NW, DEPTH, true>(a, unit, s, part, L, nullptr, kst[w]);
 }
 
-// Position in the compact item list (sequence-major, then head unit, then
-// partition) and in the blocks of the current item.
+// Streaming mode: position of a worker in the compact item list
+// (sequence-major, then head unit, then partition) and in the blocks of the
+// current item.  Every field is wave-uniform; the per-block step is one
+// increment and compare, everything else happens at item boundaries.
+//
+// The table and length pointers come from the kernel's __restrict__
+// arguments: the loop also stores results, and only loads known not to alias
+// those stores become scalar loads (a vector load of a block id would make
+// every step wait for all tile loads in flight).
 struct StreamCursor {
   int s, unit, part, nparts, len, nblocks;
-  int j, jend;     // current block, end of the item's blocks (>= j + 1)
-  int64_t item;    // index in the compact list
+  int j, jend;    // current block, end of the item's blocks (>= j + 1)
+  int left;       // items of the worker's range from the current one on
+  int kvh;        // KV head of `unit`
+  bool new_tile;  // the head tile changed at the last item boundary
+  int64_t row;    // offset of sequence s's block-table row (an offset, not a pointer:
+                  // loads must stay visibly based on the kernel argument)
+
   __device__ __forceinline__ void enter_item(const DecodeArgs& a) {
     j = part * a.part_blocks;
     jend = max(j + 1, min(j + a.part_blocks, nblocks));  // an empty context still takes a step
   }
-  __device__ __forceinline__ void enter_seq(const DecodeArgs& a) {
-    len = clamp_len(a, s);
+  __device__ __forceinline__ void enter_seq(const DecodeArgs& a, const int32_t* tables,
+                                            const int32_t* lens) {
+    len = min(max(lens[s], 0), a.max_len);
     nblocks = (len + kBlockSize - 1) / kBlockSize;
     nparts = parts_of(len, a.part_blocks);
-  }
-  // Place the cursor on item `idx` (walks the sequences).
-  __device__ __forceinline__ void seek(const DecodeArgs& a, int units, int64_t idx) {
-    int64_t cum = 0;
-    for (s = 0; s < a.num_seqs - 1; ++s) {
-      const int64_t n = (int64_t)units * parts_of(clamp_len(a, s), a.part_blocks);
-      if (idx < cum + n) break;
-      cum += n;
-    }
-    enter_seq(a);
-    const int r = (int)(idx - cum);
-    unit = r / nparts;
-    part = r % nparts;
-    item = idx;
-    enter_item(a);
+    row = (int64_t)s * a.max_blocks_per_seq;
   }
   __device__ __forceinline__ bool last_block() const { return j + 1 >= jend; }
   // Step to the next block (and item, head unit, sequence as they end).
-  __device__ __forceinline__ void advance(const DecodeArgs& a, int units) {
+  __device__ __forceinline__ void advance(const DecodeArgs& a, const int32_t* tables,
+                                          const int32_t* lens, int units, int hchunks) {
     if (++j < jend) return;
-    ++item;
+    --left;
     if (++part == nparts) {
       part = 0;
+      new_tile = true;
       if (++unit == units) {
         unit = 0;
         if (s + 1 < a.num_seqs) ++s;
-        enter_seq(a);
+        enter_seq(a, tables, lens);
       }
+      kvh = unit / hchunks;
     }
     enter_item(a);
   }
 };
+
+// Inclusive prefix sum over the 64 lanes of the wave.
+__device__ __forceinline__ int wave_inclusive_sum(int x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __builtin_amdgcn_ds_bpermute(((lane - off) & 63) << 2, x);
+    x += lane >= off ? y : 0;
+  }
+  return x;
+}
 
 // Streaming mode, for launches with many partitions and few sequences: every
 // resident wave is a worker that takes an equal contiguous share of the
@@ -509,32 +583,76 @@ struct StreamCursor {
 // load pipeline, writing each item's partial (or output row) as soon as its
 // last block is consumed.  No workgroup is ever empty, no item pays a
 // pipeline start-up, and the partitions stay exactly the ones the reduce
-// merges.
+// merges.  The launch keeps the item count below 2^31.
 template <int DT, int D, int NW, int DEPTH>
-__global__ __launch_bounds__(NW * 64) void decode_mfma_stream_kernel(DecodeArgs a) {
+#ifndef PA_STREAM_MIN_WAVES
+#define PA_STREAM_MIN_WAVES 2  // waves per SIMD the register budget must allow
+#endif
+__global__ __launch_bounds__(NW * 64, PA_STREAM_MIN_WAVES) void decode_mfma_stream_kernel(
+    DecodeArgs a, const int32_t* __restrict__ tables, const int32_t* __restrict__ lens) {
   using S = MfmaShape<DT, D>;
   using VT = typename S::VT;
+  __shared__ u32x4 kst_all[NW][kKStageSlots<D>];
   const MfmaLane ln;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int group = a.num_q_heads / a.num_kv_heads;
-  const int units = a.num_kv_heads * ((group + 15) >> 4);
+  const int hchunks = (group + 15) >> 4;
+  const int units = a.num_kv_heads * hchunks;
+  u32x4* kst = kst_all[w];
 
-  int64_t total = 0;
-  for (int s = 0; s < a.num_seqs; ++s)
-    total += (int64_t)units * parts_of(clamp_len(a, s), a.part_blocks);
-  const int64_t workers = (int64_t)gridDim.x * NW;
-  const int64_t wid = (int64_t)blockIdx.x * NW + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t i0 = total * wid / workers, i1 = total * (wid + 1) / workers;
+  // Item counts of the sequences, 64 at a time, summed across the lanes:
+  // the total, then the sequence holding this worker's first item.
+  int total = 0;
+  for (int s0 = 0; s0 < a.num_seqs; s0 += 64) {
+    const int s = s0 + lane;
+    const int n = s < a.num_seqs ? units * parts_of(min(max(lens[s], 0), a.max_len), a.part_blocks)
+                                 : 0;
+    total += __builtin_amdgcn_readlane(wave_inclusive_sum(n), 63);
+  }
+  const int workers = gridDim.x * NW;
+  const int wid = blockIdx.x * NW + w;
+  const int i0 = (int)((int64_t)total * wid / workers);
+  const int i1 = (int)((int64_t)total * (wid + 1) / workers);
   if (i0 >= i1) return;
 
-  StreamCursor lc, cc;  // load cursor (runs DEPTH-1 steps ahead), consume cursor
-  lc.seek(a, units, i0);
-  cc = lc;
+  StreamCursor lc;  // load cursor (runs DEPTH-1 steps ahead of the consume cursor)
+  {
+    int cum = 0, seq = a.num_seqs - 1;
+    for (int s0 = 0; s0 < a.num_seqs; s0 += 64) {
+      const int s = s0 + lane;
+      const int n = s < a.num_seqs
+                        ? units * parts_of(min(max(lens[s], 0), a.max_len), a.part_blocks)
+                        : 0;
+      const int incl = cum + wave_inclusive_sum(n);
+      // sequences of this chunk that end at or before item i0
+      const uint64_t done = __builtin_amdgcn_ballot_w64(s < a.num_seqs && incl <= i0);
+      const int k = __builtin_popcountll(done);
+      if (k < 64) {  // sequence s0 + k holds item i0
+        seq = s0 + k;
+        cum = k > 0 ? __builtin_amdgcn_readlane(incl, k - 1) : cum;
+        break;
+      }
+      cum = __builtin_amdgcn_readlane(incl, 63);
+    }
+    lc.s = min(seq, a.num_seqs - 1);
+    lc.enter_seq(a, tables, lens);
+    const int r = i0 - cum;
+    lc.unit = r / lc.nparts;
+    lc.part = r % lc.nparts;
+    lc.kvh = lc.unit / hchunks;
+    lc.left = i1 - i0;
+    lc.new_tile = false;
+    lc.enter_item(a);
+  }
+  StreamCursor cc = lc;  // consume cursor
+
   HeadTile t = head_tile(a, cc.unit, cc.s);
   u32x4 qb[S::NJ];
   load_q<DT, D>(a, t, ln, qb);
-  int q_s = cc.s, q_unit = cc.unit;
   MfmaState<D> st;
   st.reset();
+  int seg_part0 = cc.part;  // first partition of the open segment
 
   u32x4 kr[DEPTH][S::NJ];
   VT vr[DEPTH][4];
@@ -542,20 +660,16 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_stream_kernel(DecodeArgs 
   // Issue the loads of the load cursor's block (empty once past this
   // worker's range) and step the cursor.
   auto issue = [&](int slot, int bid) {
-    const bool live = lc.item < i1;
-    const HeadTile lt = head_tile(a, lc.unit, lc.s);
+    const bool live = lc.left > 0;
+    const bool ok = live && lc.j < lc.nblocks && (uint32_t)bid < (uint32_t)a.num_blocks_i32;
     Rsrc rk, rv;
-    tile_rsrc<DT, D>(a, bid, lt.kvh, live && lc.j < lc.nblocks, rk, rv);
-    lim[slot] = (live && (uint32_t)bid < (uint32_t)a.num_blocks_i32)
-                    ? max(0, min(kBlockSize, lc.len - lc.j * kBlockSize))
-                    : 0;
+    tile_rsrc<DT, D>(a, bid, lc.kvh, ok, rk, rv);
+    lim[slot] = ok ? min(kBlockSize, lc.len - lc.j * kBlockSize) : 0;
     load_tile<DT, D, false>(rk, rv, ln, kr[slot], vr[slot]);
-    if (live) lc.advance(a, units);
+    if (live) lc.advance(a, tables, lens, units, hchunks);
   };
   auto id_of = [&](const StreamCursor& c) -> int {
-    return (c.item < i1 && c.j < c.nblocks)
-               ? a.block_tables[(int64_t)c.s * a.max_blocks_per_seq + c.j]
-               : 0;
+    return (c.left > 0 && c.j < c.nblocks) ? tables[c.row + c.j] : 0;
   };
 
   static_for<0, DEPTH - 1>([&](auto dc) { issue(decltype(dc)::value, id_of(lc)); });
@@ -569,24 +683,38 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_stream_kernel(DecodeArgs 
       issue(dn, id);
       next_id = id_of(lc);
       if (running) {
-        if (cc.s != q_s || cc.unit != q_unit) {  // a new head tile: its query
+        if (cc.new_tile) {  // a new head tile: its query
           t = head_tile(a, cc.unit, cc.s);
           load_q<DT, D>(a, t, ln, qb);
-          q_s = cc.s;
-          q_unit = cc.unit;
+          // Wait for q here, on this rare path: left pending past the
+          // branch, it would make every step wait for all loads in flight.
+          wait_loaded(qb);
+          cc.new_tile = false;
         }
-        consume_any<DT, D>(st, qb, kr[d], vr[d], lim[d], a.scale_log2, ln);
+        consume_any<DT, D>(st, qb, kr[d], vr[d], lim[d], a.scale_log2, ln, kst);
+        bool closed = false;
         if (cc.last_block()) {
-          if (cc.len == 0) {  // empty context: zero row
-            for (int i = threadIdx.x & 63; i < t.nh * D; i += 64)
-              store_elem<DT>(a.out, t.orow0 * D + i, 0.f);
-          } else {
-            write_wave_item<DT, D>(a, st, t, cc.part, cc.nparts, ln);
+          // Consecutive partitions of one head tile in this worker's range
+          // are one segment: the softmax state runs on, and the segment's
+          // merged partial goes to the slot of its first partition, the
+          // others marked empty.  Stores are few (one partial per head tile
+          // per worker) and so are the waits that follow them.
+          const bool more = cc.left > 1;
+          if (!(more && cc.part + 1 < cc.nparts)) {
+            if (cc.len == 0) {  // empty context: zero row
+              for (int i = lane; i < t.nh * D; i += 64)
+                store_elem<DT>(a.out, t.orow0 * D + i, 0.f);
+            } else {
+              write_wave_item<DT, D>(a, st, t, seg_part0, cc.nparts, ln);
+              mark_empty(a, t, seg_part0 + 1, cc.part, ln);
+            }
+            st.reset();
+            running = more;
+            closed = true;
           }
-          st.reset();
-          running = cc.item + 1 < i1;
         }
-        cc.advance(a, units);
+        cc.advance(a, tables, lens, units, hchunks);
+        if (closed) seg_part0 = cc.part;
       }
     });
   }
@@ -613,7 +741,10 @@ hipError_t launch_shape(const DecodeArgs& a, hipStream_t stream) {
 
 // Launches with at least kWaveItemParts partitions take one wave per item;
 // with at most kStreamMaxSeqs sequences as well, the streaming mode.
-constexpr int kWaveItemParts = 8;
+#ifndef PA_WAVE_ITEM_PARTS
+#define PA_WAVE_ITEM_PARTS 8
+#endif
+constexpr int kWaveItemParts = PA_WAVE_ITEM_PARTS;
 #ifndef PA_STREAM_MAX_SEQS
 #define PA_STREAM_MAX_SEQS 64
 #endif
@@ -621,7 +752,7 @@ constexpr int kWaveItemParts = 8;
 #define PA_MFMA_STREAM_WAVES 4  // waves per workgroup, streaming mode
 #endif
 #ifndef PA_MFMA_STREAM_DEPTH
-#define PA_MFMA_STREAM_DEPTH 3  // tiles per wave in the load pipeline, streaming mode
+#define PA_MFMA_STREAM_DEPTH 2  // tiles per wave in the load pipeline, streaming mode
 #endif
 constexpr int kStreamMaxSeqs = PA_STREAM_MAX_SEQS;
 
@@ -635,25 +766,35 @@ hipError_t launch_wave_shape(const DecodeArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+#ifndef PA_STREAM_WG_PER_CU
+#define PA_STREAM_WG_PER_CU 1  // streaming workgroups per compute unit
+#endif
+
+// One streaming workgroup per compute unit (never more than are resident):
+// measured on the long-context shape, fewer workers with longer ranges beat
+// filling every wave slot, and a grid that is not a multiple of the CU count
+// leaves some CUs with twice the work.
 template <int DT, int D, int NW, int DEPTH>
-hipError_t launch_stream_shape(const DecodeArgs& a, hipStream_t stream) {
+hipError_t launch_stream_shape(const DecodeArgs& a, int64_t items, hipStream_t stream) {
   const auto kernel = decode_mfma_stream_kernel<DT, D, NW, DEPTH>;
   static ResidentCache cache;
-  const int group = a.num_q_heads / a.num_kv_heads;
-  const int64_t items = (int64_t)a.num_kv_heads * ((group + 15) / 16) * a.num_seqs *
-                        a.max_partitions;
-  const int grid = resident_workgroups(reinterpret_cast<const void*>(kernel), NW * 64, cache);
-  if (grid <= 0) return hipErrorInvalidValue;
+  const int resident = resident_workgroups(reinterpret_cast<const void*>(kernel), NW * 64, cache);
+  const int cus = compute_units();
+  if (resident <= 0 || cus <= 0) return hipErrorInvalidValue;
+  const int grid = std::min(resident, cus * PA_STREAM_WG_PER_CU);
   const int64_t need = (items + NW - 1) / NW;  // never more workers than items
   hipLaunchKernelGGL(kernel, dim3((unsigned)(need < grid ? need : grid)), dim3(NW * 64), 0,
-                     stream, a);
+                     stream, a, a.block_tables, a.context_lens);
   return hipGetLastError();
 }
 
 template <int DT, int D>
 hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
-  if (a.max_partitions >= kWaveItemParts && a.num_seqs <= kStreamMaxSeqs)
-    return launch_stream_shape<DT, D, PA_MFMA_STREAM_WAVES, PA_MFMA_STREAM_DEPTH>(a, stream);
+  const int group = a.num_q_heads / a.num_kv_heads;
+  const int64_t items = (int64_t)a.num_kv_heads * ((group + 15) / 16) * a.num_seqs *
+                        a.max_partitions;
+  if (a.max_partitions >= kWaveItemParts && a.num_seqs <= kStreamMaxSeqs && items < INT32_MAX)
+    return launch_stream_shape<DT, D, PA_MFMA_STREAM_WAVES, PA_MFMA_STREAM_DEPTH>(a, items, stream);
   if (a.max_partitions >= kWaveItemParts)
     return launch_wave_shape<DT, D, PA_MFMA_WAVE_ITEM_WAVES, PA_MFMA_WAVE_ITEM_DEPTH>(a, stream);
   return a.part_blocks >= kLongItemBlocks ? launch_shape<DT, D, 8, 2>(a, stream)

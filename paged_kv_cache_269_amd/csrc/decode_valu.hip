@@ -302,7 +302,10 @@ hipError_t launch_shape(const DecodeArgs& a, hipStream_t stream) {
 }
 
 // Launches with at least kWaveItemParts partitions take one wave per item.
-constexpr int kWaveItemParts = 8;
+#ifndef PA_WAVE_ITEM_PARTS
+#define PA_WAVE_ITEM_PARTS 8
+#endif
+constexpr int kWaveItemParts = PA_WAVE_ITEM_PARTS;
 
 template <int DT, int D, int NW, int DEPTH>
 hipError_t launch_wave_shape(const DecodeArgs& a, hipStream_t stream) {
