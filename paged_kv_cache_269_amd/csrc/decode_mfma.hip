@@ -497,7 +497,7 @@ template <int DT, int D, int NW, int DEPTH>
 __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
   __shared__ MfmaLds<D, NW> sm;
   __shared__ u32x4 kst[NW][kKStageSlots<D>];
-  const int unit = blockIdx.x, s = blockIdx.y, part = blockIdx.z;
+  const int unit = blockIdx.x, s = longest_first(a, blockIdx.y), part = blockIdx.z;
   const int L = clamp_len(a, s);
   if (part >= parts_of(L, a.part_blocks)) return;  // past this sequence's end
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -509,7 +509,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
 template <int DT, int D, int NW, int DEPTH>
 __global__ __launch_bounds__(NW * 64) void decode_mfma_wave_kernel(DecodeArgs a) {
   __shared__ u32x4 kst[NW][kKStageSlots<D>];
-  const int unit = blockIdx.x, s = blockIdx.y;
+  const int unit = blockIdx.x, s = longest_first(a, blockIdx.y);
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int part = blockIdx.z * NW + w;
   const int L = clamp_len(a, s);

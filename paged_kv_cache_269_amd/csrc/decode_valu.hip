@@ -264,7 +264,7 @@ __device__ __forceinline__ void valu_item(const DecodeArgs& a, const int h, cons
 template <int DT, int D, int NW, int DEPTH>
 __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(DecodeArgs a) {
   __shared__ ValuLds<DT, D, NW> sm;
-  const int unit = blockIdx.x, s = blockIdx.y, part = blockIdx.z;
+  const int unit = blockIdx.x, s = longest_first(a, blockIdx.y), part = blockIdx.z;
   const int L = clamp_len(a, s);
   if (part >= parts_of(L, a.part_blocks)) return;  // past this sequence's end
   valu_item<DT, D, NW, DEPTH, false>(a, unit, s, part, L, &sm);
@@ -275,7 +275,7 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(DecodeArgs a) {
 // partition; there is no cross-wave merge).
 template <int DT, int D, int NW, int DEPTH>
 __global__ __launch_bounds__(NW * 64) void decode_valu_wave_kernel(DecodeArgs a) {
-  const int unit = blockIdx.x, s = blockIdx.y;
+  const int unit = blockIdx.x, s = longest_first(a, blockIdx.y);
   const int part = blockIdx.z * NW + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int L = clamp_len(a, s);
   if (part >= parts_of(L, a.part_blocks)) return;  // past this sequence's end

@@ -20,6 +20,57 @@ __device__ __forceinline__ int parts_of(int L, int part_blocks) {
   return P > 0 ? P : 1;
 }
 
+// Sequence that grid slot `slot` works on.  The hardware dispatcher starts
+// workgroups in grid order, so slots take the sequences in decreasing order
+// of context length (ties by index): the longest items start first and the
+// last to start are the shortest, which keeps the tail of the launch short
+// (longest-processing-time-first list scheduling).  Each wave finds its
+// sequence by bisection on the length, counting with ballots over the
+// lengths held in registers.  Launches with more than kOrderMaxSeqs
+// sequences keep the grid order.
+constexpr int kOrderMaxSeqs = 256;
+
+__device__ __forceinline__ int longest_first(const DecodeArgs& a, int slot) {
+  if (a.num_seqs > kOrderMaxSeqs) return slot;
+  const int lane = threadIdx.x & 63;
+  constexpr int kChunks = kOrderMaxSeqs / 64;
+  int len[kChunks];
+#pragma unroll
+  for (int c = 0; c < kChunks; ++c) {
+    const int s = c * 64 + lane;
+    len[c] = s < a.num_seqs ? clamp_len(a, s) : -1;
+  }
+  auto count_ge = [&](int v) {
+    int n = 0;
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) n += __builtin_popcountll(__builtin_amdgcn_ballot_w64(len[c] >= v));
+    return n;
+  };
+  // largest length v with at least slot + 1 sequences of length >= v
+  int lo = 0, hi = a.max_len;
+  while (lo < hi) {
+    const int mid = lo + (hi - lo + 1) / 2;
+    if (count_ge(mid) > slot)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  int r = slot - count_ge(lo + 1);  // rank among the sequences of length lo, by index
+#pragma unroll
+  for (int c = 0; c < kChunks; ++c) {
+    const uint64_t m = __builtin_amdgcn_ballot_w64(len[c] == lo);
+    const int k = __builtin_popcountll(m);
+    if (r < k) {
+      const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+      const uint64_t hit = __builtin_amdgcn_ballot_w64(((m >> lane) & 1) && below == r);
+      return c * 64 + __builtin_ctzll(hit);
+    }
+    r -= k;
+  }
+  return slot;  // not reached: slot < num_seqs
+}
+
 // Host: compute units of the current device (cached per device; <= 0 on a
 // runtime error).
 inline int compute_units() {
