@@ -58,8 +58,8 @@ def kernel_source_hash() -> str:
     """Hash of the decode kernel sources, to tell whether stored counters
     still describe the code being run."""
     h = hashlib.sha256()
-    for f in ("common.h", "items.h", "launch.h", "decode_valu.hip", "decode_mfma.hip",
-              "reduce.hip", "api.cpp"):
+    for f in ("common.h", "items.h", "launch.h", "mfma_tile.h", "decode_valu.hip",
+              "decode_mfma.hip", "prefix.hip", "reduce.hip", "api.cpp"):
         with open(os.path.join(ROOT, "paged_kv_cache_269_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -144,8 +144,12 @@ def main(argv=None) -> int:
     for _ in range(max(1, args.pool_copies) - 1):
         pools.append((d["k_cache"].clone(), d["v_cache"].clone()))
     out = torch.empty_like(d["q"])
-    ws = pa.decode_workspace(w.num_seqs, w.num_q_heads, w.head_dim, w.max_context_len, part,
-                             device=dev)   # allocated once, outside the timed loop
+    cascade = bool(w.params.get("cascade")) and part == 0
+    if cascade:   # allocated once, outside the timed loop
+        ws = pa.cascade_workspace(w.num_seqs, w.num_q_heads, w.head_dim, device=dev)
+    else:
+        ws = pa.decode_workspace(w.num_seqs, w.num_q_heads, w.head_dim, w.max_context_len, part,
+                                 device=dev)
     stream = torch.cuda.current_stream()
 
     def reshape(i):
@@ -154,9 +158,14 @@ def main(argv=None) -> int:
 
     def decode(i):
         kc, vc = pools[i % len(pools)]
-        pa.paged_attention_decode(out, d["q"], kc, vc, d["block_tables"], d["context_lens"],
-                                  w.scale, w.max_context_len, partition_size=part, workspace=ws,
-                                  stream=stream)
+        if cascade:
+            pa.paged_attention_decode_cascade(out, d["q"], kc, vc, d["block_tables"],
+                                              d["context_lens"], w.scale, w.max_context_len,
+                                              workspace=ws, stream=stream)
+        else:
+            pa.paged_attention_decode(out, d["q"], kc, vc, d["block_tables"], d["context_lens"],
+                                      w.scale, w.max_context_len, partition_size=part,
+                                      workspace=ws, stream=stream)
 
     if args.calibration_copy_mib > 0:
         n = args.calibration_copy_mib << 18           # float32 elements
@@ -216,6 +225,8 @@ def main(argv=None) -> int:
                    "context_len_mean": float(w.context_lens.mean()),
                    "context_len_max": int(w.max_context_len), "num_blocks": w.num_blocks,
                    "pool_copies": len(pools),
+                   "entry": ("pa_paged_attention_decode_cascade" if cascade
+                             else "pa_paged_attention_decode"),
                    "step": ("decode" if args.decode_only else "reshape_and_cache + decode")
                            + (" + split-K reduce" if part and w.max_context_len > part else "")},
         "seqs_per_s": round(w.num_seqs / (ms_per_step * 1e-3), 1),
@@ -225,9 +236,11 @@ def main(argv=None) -> int:
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic,
-                     "kernel": "pa_paged_attention_decode (decode kernel"
-                               + (" + split-K reduce" if part and w.max_context_len > part
-                                  else "") + ")",
+                     "kernel": ("pa_paged_attention_decode_cascade (shared-prefix kernel + "
+                                "decode kernel)" if cascade else
+                                "pa_paged_attention_decode (decode kernel"
+                                + (" + split-K reduce" if part and w.max_context_len > part
+                                   else "") + ")"),
                      "launch_us_avg": round(dec_avg * 1e3, 2),
                      "launch_us_p10": round(float(np.percentile(dec_ms, 10)) * 1e3, 2),
                      "launch_us_p90": round(float(np.percentile(dec_ms, 90)) * 1e3, 2),

@@ -9,12 +9,14 @@
  *        cache cut into fixed 16-token pages found through a per-request page
  *        table, pages anywhere in memory and shareable between requests;
  *        §2.2 cache layout [num_pages, num_heads, page_size, head_dim] and
- *        the in-pool token address page_id * BLOCK_SIZE + page_offset.
+ *        the in-pool token address page_id * BLOCK_SIZE + page_offset;
+ *        §2.3 requests sharing a prompt prefix map the same pages.
  *   [MJ] vLLM tutorial (mjmagnets.cn/news/49643), §2.2: the attention op
  *        gathers K and V blocks named by the block table, then computes.
  *   [DM] vLLM project manual (doramagic.ai/projects/vllm/manual), PagedAttention
  *        V1/V2 kernels: paged KV reads, wavefront-level reductions, fused
- *        kernel, wide vector loads.
+ *        kernel, wide vector loads; KV cache manager: reference-counted
+ *        blocks shared between requests ("sharing mechanism").
  *
  * Common conventions
  *   - Element types (dtype): PA_F32, PA_F16 (IEEE binary16), PA_BF16.  q,
@@ -64,7 +66,8 @@ enum pa_status {
                              num_q_heads % num_kv_heads != 0 */
   PA_ERR_UNSUPPORTED = 3, /* head_dim not 64/128, block_size not 16, unknown dtype,
                              partition_size not a positive multiple of 16 (or 0) */
-  PA_ERR_WORKSPACE = 4,   /* workspace missing or smaller than pa_decode_workspace_bytes */
+  PA_ERR_WORKSPACE = 4,   /* workspace missing or smaller than pa_decode_workspace_bytes
+                             (pa_cascade_workspace_bytes for the cascade entry point) */
   PA_ERR_RANGE = 5,       /* host table check: an entry, length or slot out of range */
   PA_ERR_LAUNCH = 6       /* the HIP runtime refused a launch */
 };
@@ -146,6 +149,42 @@ int pa_paged_attention_reduce(void* out, const float* max_logits, const float* e
  */
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                                  int32_t max_context_len, int32_t partition_size);
+
+/*
+ * Cascade decode, for batches whose sequences share prompt pages ([CX] §2.1
+ * and §2.3: several sequences' tables point at the same physical blocks;
+ * [DM] "sharing mechanism").  Same result as pa_paged_attention_decode with
+ * partition_size = 0, computed in two parts.  Runs of 16 / G consecutive
+ * sequences (G = num_q_heads / num_kv_heads; runs start at sequence 0) whose
+ * tables begin with the same physical blocks -- whole blocks inside every
+ * member's context, at least 4 of them -- get the attention over those
+ * blocks once for the whole run, the query rows of all members in one
+ * matrix-core tile; each sequence's remaining blocks are then processed as in
+ * pa_paged_attention_decode and the two parts merged by the log-sum-exp rule
+ * of pa_paged_attention_reduce.  Runs that share fewer blocks are decoded as
+ * usual; float32, G > 8 or num_seqs < 2 skip the shared part altogether.
+ *
+ * `workspace` (device memory, caller-owned) must hold at least
+ * pa_cascade_workspace_bytes(num_seqs, num_q_heads, head_dim) bytes: it
+ * carries the shared part's per-row state from the first kernel to the
+ * second.  Calls that share a workspace must not run concurrently.  Other
+ * arguments, layouts and errors as for pa_paged_attention_decode.
+ */
+int pa_paged_attention_decode_cascade(void* out, const void* q, const void* k_cache,
+                                      const void* v_cache, const int32_t* block_tables,
+                                      const int32_t* context_lens, int32_t num_seqs,
+                                      int32_t num_q_heads, int32_t num_kv_heads,
+                                      int32_t head_dim, int32_t block_size,
+                                      int32_t max_blocks_per_seq, int64_t num_blocks,
+                                      float scale, int32_t dtype, int32_t max_context_len,
+                                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Workspace bytes of pa_paged_attention_decode_cascade: one int32 per
+ * sequence, and per (sequence, query head) row two floats plus head_dim
+ * floats, each array 256-byte aligned.  Returns 0 for invalid arguments.
+ */
+size_t pa_cascade_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim);
 
 /*
  * Host-side check of block tables (host pointers): every entry a sequence

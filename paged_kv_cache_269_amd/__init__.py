@@ -8,11 +8,14 @@ and raises if the library is missing -- there is no fallback path.
 """
 from ._binding import (  # noqa: F401
     PagedAttnError,
+    cascade_workspace,
+    cascade_workspace_bytes,
     decode_workspace,
     decode_workspace_bytes,
     lib_path,
     load_library,
     paged_attention_decode,
+    paged_attention_decode_cascade,
     paged_attention_reduce,
     reshape_and_cache,
     status_string,
@@ -23,8 +26,8 @@ from ._binding import (  # noqa: F401
 )
 
 __all__ = [
-    "PagedAttnError", "decode_workspace", "decode_workspace_bytes", "lib_path",
-    "load_library",
-    "paged_attention_decode", "paged_attention_reduce", "reshape_and_cache",
+    "PagedAttnError", "cascade_workspace", "cascade_workspace_bytes", "decode_workspace",
+    "decode_workspace_bytes", "lib_path", "load_library", "paged_attention_decode",
+    "paged_attention_decode_cascade", "paged_attention_reduce", "reshape_and_cache",
     "status_string", "validate_slots_host", "validate_tables_host", "version", "EXPORTS",
 ]

@@ -32,6 +32,10 @@ EXPORTS = {
     "pa_paged_attention_reduce": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32,
                                                  _I32, _I32, _P]),
     "pa_decode_workspace_bytes": (ctypes.c_size_t, [_I32, _I32, _I32, _I32, _I32]),
+    "pa_paged_attention_decode_cascade": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I32, _I32,
+                                                         _I32, _I32, _I32, _I32, _I64, _F32,
+                                                         _I32, _I32, _P, _SZ, _P]),
+    "pa_cascade_workspace_bytes": (ctypes.c_size_t, [_I32, _I32, _I32]),
     "pa_validate_tables_host": (ctypes.c_int, [_P, _P, _I32, _I32, _I64, _I32]),
     "pa_validate_slots_host": (ctypes.c_int, [_P, _I32, _I64, _I32]),
     "pa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -167,6 +171,45 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
         block_tables.shape[1], N, float(scale), _dtype_code(q), int(partition_size),
         int(max_context_len), ws_ptr, ws_bytes, _stream_handle(stream))
     _check("pa_paged_attention_decode", rc)
+
+
+def cascade_workspace_bytes(num_seqs: int, num_q_heads: int, head_dim: int) -> int:
+    return int(load_library().pa_cascade_workspace_bytes(num_seqs, num_q_heads, head_dim))
+
+
+def cascade_workspace(num_seqs: int, num_q_heads: int, head_dim: int, device="cuda"):
+    """A uint8 workspace tensor for paged_attention_decode_cascade."""
+    import torch
+    n = cascade_workspace_bytes(num_seqs, num_q_heads, head_dim)
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=device)
+
+
+def paged_attention_decode_cascade(out, q, k_cache, v_cache, block_tables, context_lens,
+                                   scale: float, max_context_len: int, workspace=None,
+                                   stream=None) -> None:
+    """One-pass decode that computes blocks shared by runs of consecutive
+    sequences once per run (same result as paged_attention_decode with
+    partition_size=0).  ``workspace``: at least cascade_workspace_bytes(...)
+    bytes; allocated here when omitted."""
+    import torch
+    B, Hq, D = q.shape
+    N, Hkv, bs, D2 = k_cache.shape
+    if out.shape != q.shape or D2 != D or v_cache.shape != k_cache.shape:
+        raise ValueError("shape mismatch between q, out and the caches")
+    if not (q.dtype == out.dtype == k_cache.dtype == v_cache.dtype):
+        raise TypeError("q, out and caches must share one element type")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.shape != (B,):
+        raise ValueError("block_tables must be [num_seqs, max_blocks], context_lens [num_seqs]")
+    if workspace is None:
+        workspace = cascade_workspace(B, Hq, D, q.device)
+    rc = load_library().pa_paged_attention_decode_cascade(
+        _dev_ptr(out, "out"), _dev_ptr(q, "q"), _dev_ptr(k_cache, "k_cache"),
+        _dev_ptr(v_cache, "v_cache"), _dev_ptr(block_tables, "block_tables", torch.int32),
+        _dev_ptr(context_lens, "context_lens", torch.int32), B, Hq, Hkv, D, bs,
+        block_tables.shape[1], N, float(scale), _dtype_code(q), int(max_context_len),
+        _dev_ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _stream_handle(stream))
+    _check("pa_paged_attention_decode_cascade", rc)
 
 
 def paged_attention_reduce(out, max_logits, exp_sums, tmp_out, context_lens,

@@ -14,11 +14,14 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["api.cpp", "reshape_and_cache.hip", "decode_valu.hip", "decode_mfma.hip",
-           "reduce.hip"]
+           "prefix.hip", "reduce.hip"]
 
-# Packed fp32 ALU ops are kept out of the generated code.
+# Packed fp32 ALU ops are kept out of the generated code.  Matrix-core
+# accumulators are kept in ordinary VGPRs: the online-softmax rescale works on
+# them with vector ALU ops, which cannot read accumulation registers.
 COMMON_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
                 "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                "-mllvm", "-amdgpu-mfma-vgpr-form=1",
                 "-Wall", "-I", os.path.join(ROOT, "include")]
 
 

@@ -51,6 +51,131 @@ WsLayout ws_layout(int64_t num_seqs, int64_t heads, int64_t head_dim, int64_t pa
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Shared-prefix state layout: [prefix_blocks (B) int32 | m (B Hq) | l (B Hq) |
+// o (B Hq D)], each 256-byte aligned.
+struct CascadeLayout {
+  size_t prefix_blocks = 0, m = 0, l = 0, o = 0, total = 0;
+};
+
+CascadeLayout cascade_layout(int64_t num_seqs, int64_t heads, int64_t head_dim) {
+  CascadeLayout c;
+  const size_t rows = (size_t)num_seqs * heads;
+  c.m = align256((size_t)num_seqs * sizeof(int32_t));
+  c.l = c.m + align256(rows * sizeof(float));
+  c.o = c.l + align256(rows * sizeof(float));
+  c.total = c.o + align256(rows * head_dim * sizeof(float));
+  return c;
+}
+
+// The largest query-head group the shared-prefix kernel handles (16 / G
+// sequences per matrix-core tile).
+constexpr int kCascadeMaxGroup = 8;
+
+int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cache,
+                const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+                int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                int32_t max_blocks_per_seq, int64_t num_blocks, float scale, int32_t dtype,
+                int32_t partition_size, int32_t max_context_len, void* workspace,
+                size_t workspace_bytes, void* stream, bool cascade);
+
+}  // namespace
+
+namespace {
+
+int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cache,
+                const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+                int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                int32_t max_blocks_per_seq, int64_t num_blocks, float scale, int32_t dtype,
+                int32_t partition_size, int32_t max_context_len, void* workspace,
+                size_t workspace_bytes, void* stream, bool cascade) {
+  if (!elem_bytes(dtype) || block_size != kBlock || !head_dim_ok(head_dim))
+    return PA_ERR_UNSUPPORTED;
+  if (partition_size < 0 || partition_size % kBlock) return PA_ERR_UNSUPPORTED;
+  if (num_seqs < 0 || num_seqs > kMaxGridYZ || num_q_heads <= 0 || num_q_heads > kMaxGridYZ ||
+      num_kv_heads <= 0 || num_q_heads % num_kv_heads || max_blocks_per_seq <= 0 ||
+      num_blocks <= 0 || max_context_len < 0)
+    return PA_ERR_SHAPE;
+  if (num_seqs == 0) return PA_OK;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return PA_ERR_NULL;
+
+  // Longest context any kernel will look at.
+  const int64_t max_len = std::min<int64_t>(max_context_len, (int64_t)max_blocks_per_seq * kBlock);
+  const int64_t table_blocks = ceil_div(std::max<int64_t>(max_len, 1), kBlock);
+  int64_t part_blocks, parts;
+  if (partition_size == 0) {
+    part_blocks = table_blocks;
+    parts = 1;
+  } else {
+    part_blocks = partition_size / kBlock;
+    parts = std::max<int64_t>(1, ceil_div(max_len, partition_size));
+  }
+  if (parts > kMaxGridYZ) return PA_ERR_SHAPE;  // partitions are a grid dimension
+
+  const WsLayout ws = ws_layout(num_seqs, num_q_heads, head_dim, parts);
+  if (ws.total && (!workspace || workspace_bytes < ws.total)) return PA_ERR_WORKSPACE;
+  const CascadeLayout cl = cascade_layout(num_seqs, num_q_heads, head_dim);
+  if (cascade && (!workspace || workspace_bytes < cl.total)) return PA_ERR_WORKSPACE;
+
+  pa::DecodeArgs a{};
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  char* wsb = static_cast<char*>(workspace);
+  a.tmp_out = parts > 1 ? reinterpret_cast<float*>(wsb + ws.tmp_out) : nullptr;
+  a.max_logits = parts > 1 ? reinterpret_cast<float*>(wsb + ws.max_logits) : nullptr;
+  a.exp_sums = parts > 1 ? reinterpret_cast<float*>(wsb + ws.exp_sums) : nullptr;
+  a.num_seqs = num_seqs;
+  a.num_blocks_i32 = (int)std::min<int64_t>(num_blocks, INT32_MAX);
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.max_len = (int)max_len;
+  a.part_blocks = (int)part_blocks;
+  a.max_partitions = (int)parts;
+  a.scale_log2 = scale * 1.4426950408889634f;
+
+  const hipStream_t st = (hipStream_t)stream;
+  const int group = num_q_heads / num_kv_heads;
+  // Grouped heads share every K/V tile: a matrix-core product pays off from
+  // two heads up.  Single heads and fp32 stay on the vector ALU.
+  const bool use_mfma = dtype != PA_F32 && group >= PA_MFMA_MIN_GROUP;
+  if (cascade && dtype != PA_F32 && group <= kCascadeMaxGroup && num_seqs >= 2) {
+    // Shared-prefix pass first; the decode kernel then covers each
+    // sequence's remaining blocks and merges the two parts.
+    char* c = static_cast<char*>(workspace);
+    pa::PrefixOut po{reinterpret_cast<int32_t*>(c + cl.prefix_blocks),
+                     reinterpret_cast<float*>(c + cl.m), reinterpret_cast<float*>(c + cl.l),
+                     reinterpret_cast<float*>(c + cl.o)};
+    a.prefix_blocks = po.prefix_blocks;
+    a.prefix_m = po.m;
+    a.prefix_l = po.l;
+    a.prefix_o = po.o;
+    if (pa::launch_prefix(a, po, dtype, head_dim, st) != hipSuccess) return PA_ERR_LAUNCH;
+  }
+  hipError_t e = use_mfma ? pa::launch_decode_mfma(a, dtype, head_dim, st)
+                          : pa::launch_decode_valu(a, dtype, head_dim, st);
+  if (e != hipSuccess) return PA_ERR_LAUNCH;
+  if (parts > 1) {
+    pa::ReduceArgs r{};
+    r.out = out;
+    r.max_logits = a.max_logits;
+    r.exp_sums = a.exp_sums;
+    r.tmp_out = a.tmp_out;
+    r.context_lens = context_lens;
+    r.num_q_heads = num_q_heads;
+    r.partition_size = partition_size;
+    r.max_partitions = (int)parts;
+    r.max_len = (int)max_len;
+    r.skip_single = 1;
+    e = pa::launch_reduce(r, dtype, head_dim, num_seqs, st);
+    if (e != hipSuccess) return PA_ERR_LAUNCH;
+  }
+  return PA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -101,77 +226,28 @@ int pa_paged_attention_decode(void* out, const void* q, const void* k_cache, con
                               int64_t num_blocks, float scale, int32_t dtype,
                               int32_t partition_size, int32_t max_context_len, void* workspace,
                               size_t workspace_bytes, void* stream) {
-  if (!elem_bytes(dtype) || block_size != kBlock || !head_dim_ok(head_dim))
-    return PA_ERR_UNSUPPORTED;
-  if (partition_size < 0 || partition_size % kBlock) return PA_ERR_UNSUPPORTED;
-  if (num_seqs < 0 || num_seqs > kMaxGridYZ || num_q_heads <= 0 || num_q_heads > kMaxGridYZ ||
-      num_kv_heads <= 0 || num_q_heads % num_kv_heads || max_blocks_per_seq <= 0 ||
-      num_blocks <= 0 || max_context_len < 0)
-    return PA_ERR_SHAPE;
-  if (num_seqs == 0) return PA_OK;
-  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return PA_ERR_NULL;
+  return decode_impl(out, q, k_cache, v_cache, block_tables, context_lens, num_seqs, num_q_heads,
+                     num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks, scale,
+                     dtype, partition_size, max_context_len, workspace, workspace_bytes, stream,
+                     false);
+}
 
-  // Longest context any kernel will look at.
-  const int64_t max_len = std::min<int64_t>(max_context_len, (int64_t)max_blocks_per_seq * kBlock);
-  const int64_t table_blocks = ceil_div(std::max<int64_t>(max_len, 1), kBlock);
-  int64_t part_blocks, parts;
-  if (partition_size == 0) {
-    part_blocks = table_blocks;
-    parts = 1;
-  } else {
-    part_blocks = partition_size / kBlock;
-    parts = std::max<int64_t>(1, ceil_div(max_len, partition_size));
-  }
-  if (parts > kMaxGridYZ) return PA_ERR_SHAPE;  // partitions are a grid dimension
+size_t pa_cascade_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim) {
+  if (num_seqs < 0 || num_q_heads <= 0 || head_dim <= 0) return 0;
+  return cascade_layout(num_seqs, num_q_heads, head_dim).total;
+}
 
-  const WsLayout ws = ws_layout(num_seqs, num_q_heads, head_dim, parts);
-  if (ws.total && (!workspace || workspace_bytes < ws.total)) return PA_ERR_WORKSPACE;
-
-  pa::DecodeArgs a{};
-  a.out = out;
-  a.q = q;
-  a.k_cache = k_cache;
-  a.v_cache = v_cache;
-  a.block_tables = block_tables;
-  a.context_lens = context_lens;
-  char* wsb = static_cast<char*>(workspace);
-  a.tmp_out = parts > 1 ? reinterpret_cast<float*>(wsb + ws.tmp_out) : nullptr;
-  a.max_logits = parts > 1 ? reinterpret_cast<float*>(wsb + ws.max_logits) : nullptr;
-  a.exp_sums = parts > 1 ? reinterpret_cast<float*>(wsb + ws.exp_sums) : nullptr;
-  a.num_seqs = num_seqs;
-  a.num_blocks_i32 = (int)std::min<int64_t>(num_blocks, INT32_MAX);
-  a.num_q_heads = num_q_heads;
-  a.num_kv_heads = num_kv_heads;
-  a.max_blocks_per_seq = max_blocks_per_seq;
-  a.max_len = (int)max_len;
-  a.part_blocks = (int)part_blocks;
-  a.max_partitions = (int)parts;
-  a.scale_log2 = scale * 1.4426950408889634f;
-
-  const hipStream_t st = (hipStream_t)stream;
-  const int group = num_q_heads / num_kv_heads;
-  // Grouped heads share every K/V tile: a matrix-core product pays off from
-  // two heads up.  Single heads and fp32 stay on the vector ALU.
-  const bool use_mfma = dtype != PA_F32 && group >= PA_MFMA_MIN_GROUP;
-  hipError_t e = use_mfma ? pa::launch_decode_mfma(a, dtype, head_dim, st)
-                          : pa::launch_decode_valu(a, dtype, head_dim, st);
-  if (e != hipSuccess) return PA_ERR_LAUNCH;
-  if (parts > 1) {
-    pa::ReduceArgs r{};
-    r.out = out;
-    r.max_logits = a.max_logits;
-    r.exp_sums = a.exp_sums;
-    r.tmp_out = a.tmp_out;
-    r.context_lens = context_lens;
-    r.num_q_heads = num_q_heads;
-    r.partition_size = partition_size;
-    r.max_partitions = (int)parts;
-    r.max_len = (int)max_len;
-    r.skip_single = 1;
-    e = pa::launch_reduce(r, dtype, head_dim, num_seqs, st);
-    if (e != hipSuccess) return PA_ERR_LAUNCH;
-  }
-  return PA_OK;
+int pa_paged_attention_decode_cascade(void* out, const void* q, const void* k_cache,
+                                      const void* v_cache, const int32_t* block_tables,
+                                      const int32_t* context_lens, int32_t num_seqs,
+                                      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                      int32_t block_size, int32_t max_blocks_per_seq,
+                                      int64_t num_blocks, float scale, int32_t dtype,
+                                      int32_t max_context_len, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+  return decode_impl(out, q, k_cache, v_cache, block_tables, context_lens, num_seqs, num_q_heads,
+                     num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks, scale,
+                     dtype, 0, max_context_len, workspace, workspace_bytes, stream, true);
 }
 
 int pa_paged_attention_reduce(void* out, const float* max_logits, const float* exp_sums,

@@ -82,8 +82,11 @@ __device__ __forceinline__ void valu_item(const DecodeArgs& a, const int h, cons
   const char* kbase = static_cast<const char*>(a.k_cache);
   const char* vbase = static_cast<const char*>(a.v_cache);
   const int32_t* __restrict__ bt = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
-  const int jb = part * a.part_blocks;
-  const int je = min(jb + a.part_blocks, nblocks);
+  // Shared-prefix launches (one pass): the leading `pre` blocks were done by
+  // the prefix kernel; their state joins the merge below.
+  const int pre = (!WAVE_ITEM && a.prefix_blocks != nullptr) ? a.prefix_blocks[s] : 0;
+  const int jb = max(part * a.part_blocks, pre);
+  const int je = min(part * a.part_blocks + a.part_blocks, nblocks);
   constexpr int STRIDE = WAVE_ITEM ? 1 : NW;
   const int j0 = jb + (WAVE_ITEM ? 0 : w);                         // blocks j0, j0+STRIDE, ...
   const int nk = je > j0 ? (je - j0 + STRIDE - 1) / STRIDE : 0;  // how many
@@ -232,8 +235,10 @@ __device__ __forceinline__ void valu_item(const DecodeArgs& a, const int h, cons
   for (int k = 0; k < VEC; ++k) sm->acc[r * D + c * VEC + k] = acc[k];
   __syncthreads();
 
+  const float pm = pre > 0 ? a.prefix_m[orow] : -INFINITY;
+  const float pl = pre > 0 ? a.prefix_l[orow] : 0.f;
   for (int d = threadIdx.x; d < D; d += NW * 64) {
-    float M = -INFINITY;
+    float M = pm;
 #pragma unroll
     for (int i = 0; i < R; ++i) M = __builtin_fmaxf(M, sm->m[i]);
     float lsum = 0.f, o = 0.f;
@@ -242,6 +247,11 @@ __device__ __forceinline__ void valu_item(const DecodeArgs& a, const int h, cons
       const float f = (sm->m[i] == -INFINITY) ? 0.f : fast_exp2(sm->m[i] - M);
       lsum += sm->l[i] * f;
       o += sm->acc[i * D + d] * f;
+    }
+    if (pre > 0) {
+      const float wp = pl * fast_exp2(pm - M);
+      lsum += wp;
+      o += wp * a.prefix_o[orow * D + d];
     }
     o = lsum > 0.f ? o / lsum : 0.f;
     if (nparts <= 1) {
@@ -315,8 +325,18 @@ hipError_t launch_wave_shape(const DecodeArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+#ifndef PA_CASCADE_WAVES
+#define PA_CASCADE_WAVES 2  // waves per item after a shared-prefix pass
+#endif
+#ifndef PA_CASCADE_DEPTH
+#define PA_CASCADE_DEPTH 2
+#endif
+
 template <int DT, int D>
 hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
+  // After a shared-prefix pass the items hold only the private blocks.
+  if (a.prefix_blocks != nullptr)
+    return launch_shape<DT, D, PA_CASCADE_WAVES, PA_CASCADE_DEPTH>(a, stream);
   if (a.max_partitions >= kWaveItemParts) return launch_wave_shape<DT, D, PA_WAVE_ITEM_WAVES, PA_WAVE_ITEM_DEPTH>(a, stream);
   return a.part_blocks >= kLongItemBlocks ? launch_shape<DT, D, 8, 3>(a, stream)
                                           : launch_shape<DT, D, 4, 2>(a, stream);

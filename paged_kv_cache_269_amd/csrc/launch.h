@@ -26,6 +26,21 @@ struct DecodeArgs {
   int part_blocks;              // blocks per partition
   int max_partitions;           // P (partials stride)
   float scale_log2;             // scale * log2(e)
+  // Shared-prefix launches: per sequence, the leading blocks whose attention
+  // the prefix kernel has already computed (nullptr: none), and that part's
+  // state per (sequence, query head) row.
+  const int32_t* prefix_blocks;  // [B]
+  const float* prefix_m;         // [B, Hq] max score, base 2
+  const float* prefix_l;         // [B, Hq] sum of exp2(score - max)
+  const float* prefix_o;         // [B, Hq, D] normalised output of the prefix part
+};
+
+// Outputs of the shared-prefix kernel (the same arrays DecodeArgs reads).
+struct PrefixOut {
+  int32_t* prefix_blocks;
+  float* m;
+  float* l;
+  float* o;
 };
 
 struct ReduceArgs {
@@ -52,6 +67,12 @@ hipError_t launch_decode_valu(const DecodeArgs& a, int dtype, int head_dim, hipS
 // Matrix-core decode for grouped heads: one workgroup per (kv head x 16-head
 // tile, sequence, partition) item.
 hipError_t launch_decode_mfma(const DecodeArgs& a, int dtype, int head_dim, hipStream_t stream);
+
+// Shared-prefix pass: for runs of consecutive sequences whose block tables
+// start with the same full blocks, the attention over those blocks, once per
+// run (f16/bf16, at most 8 query heads per KV head).
+hipError_t launch_prefix(const DecodeArgs& a, const PrefixOut& o, int dtype, int head_dim,
+                         hipStream_t stream);
 
 hipError_t launch_reduce(const ReduceArgs& a, int dtype, int head_dim, int num_seqs,
                          hipStream_t stream);

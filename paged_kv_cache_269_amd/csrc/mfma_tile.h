@@ -1,0 +1,273 @@
+// Matrix-core tile primitives shared by the decode and shared-prefix kernels.
+//
+// Per 16-token block and KV head, with up to 16 query rows sharing the tile
+// (the G query heads of a KV head, or the same head of sequences that share
+// the block): S = K_blk (16 x D) . Q^T (D x 16 rows) and
+// O += P (16 rows x 16 tokens) . V_blk (16 x D), both on MFMA:
+//   S:  v_mfma_f32_16x16x32_{bf16,f16}, D/32 of them (rows = tokens,
+//       columns = query rows, contraction over head_dim);
+//   PV: v_mfma_f32_16x16x16_{bf16,f16}, D/16 of them (rows = query rows,
+//       columns = output dims, contraction over the block's 16 tokens).
+//
+// Lane layouts (wave64, lane l, n = l % 16, g = l / 16):
+//   MFMA 16x16xK operand A: row n, contraction slice g;  B: column n, slice g;
+//   16x16 result: column n, rows 4g .. 4g+3.
+// Orders are chosen so that the products chain without moving data:
+//   * result row r of S stands for token tau(r) = r/4 + 4 (r%4), so lane l
+//     ends up with the scores of tokens g + 4e (e = 0..3) for query row n --
+//     exactly the P operand layout of the PV product (row = query row n,
+//     contraction slice g = tokens g + 4e);
+//   * the PV contraction over tokens uses the same order, so lane l needs
+//     V rows g + 4e: four wave-wide loads of 4 whole rows each (coalesced 1 KiB
+//     per instruction at D = 128), and output column n of PV product jj is
+//     dim EPL*n + jj, the elements the lane loaded;
+//   * the S contraction over head_dim visits 16-byte chunk 4j + g of a row in
+//     product j (Q is read in the same order).  K is loaded as whole
+//     contiguous KiB runs and reaches that layout through a per-wave LDS tile.
+// Online softmax runs per query row in base 2; the running max of a row lives
+// in the 4 lanes with that n, the output rows 4g..4g+3 fetch their rescale
+// factor with a lane shuffle.
+#pragma once
+
+#include <type_traits>
+
+#include "common.h"
+#include "launch.h"
+
+namespace pa {
+
+template <int DT>
+__device__ __forceinline__ f32x4 mfma_qk(const u32x4& a, const u32x4& b, const f32x4& c) {
+  if constexpr (DT == kBF16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+template <int DT>
+__device__ __forceinline__ f32x4 mfma_pv(const u32x2& a, const u32x2& b, const f32x4& c) {
+  if constexpr (DT == kBF16)
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a),
+                                                     __builtin_bit_cast(i16x4, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a),
+                                                 __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
+}
+
+// Two floats -> packed pair of 16-bit elements (round to nearest even).
+template <int DT>
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  return (uint32_t)to_bits16<DT>(lo) | ((uint32_t)to_bits16<DT>(hi) << 16);
+}
+
+// 16-bit element k of a row slice held as EPL elements.
+template <int EPL>
+struct VSlice;
+template <>
+struct VSlice<8> {
+  using T = u32x4;
+  template <bool SHARED>
+  __device__ static __forceinline__ T load(Rsrc r, int off) { return buf_load16<SHARED>(r, off); }
+  __device__ static __forceinline__ uint32_t half(const T& v, int k) {
+    return (k & 1) ? (v[k >> 1] >> 16) : (v[k >> 1] & 0xffffu);
+  }
+};
+template <>
+struct VSlice<4> {
+  using T = u32x2;
+  template <bool SHARED>
+  __device__ static __forceinline__ T load(Rsrc r, int off) { return buf_load8<SHARED>(r, off); }
+  __device__ static __forceinline__ uint32_t half(const T& v, int k) {
+    return (k & 1) ? (v[k >> 1] >> 16) : (v[k >> 1] & 0xffffu);
+  }
+};
+
+
+// LDS of a workgroup whose NW waves share one item: per wave and query row
+// the running max, sum and P.V accumulators; merge factors and totals.
+// `fp` is the weight of an earlier (shared-prefix) part of the row.
+template <int D, int NW>
+struct MfmaLds {
+  float m[NW][16], l[NW][16], f[NW][16], fp[16], tot[16], mx[16];
+  float o[NW][16][D];
+};
+
+// Shapes of one (block, KV head) tile for the matrix-core path.
+template <int DT, int D>
+struct MfmaShape {
+  static constexpr int NJ = D / 32;   // S products per block
+  static constexpr int EPL = D / 16;  // V elements per lane per row = PV products
+  static constexpr int CPR = D / 8;   // 16-byte chunks per row
+  static constexpr int TILE_BYTES = kBlockSize * D * 2;
+  using VS = VSlice<EPL>;
+  using VT = typename VS::T;
+};
+
+// Lane coordinates inside the wave.
+struct MfmaLane {
+  int n, g, tok_k;  // column/row n, contraction slice g, token of S row n
+  __device__ __forceinline__ MfmaLane() {
+    const int lane = threadIdx.x & 63;
+    n = lane & 15;
+    g = lane >> 4;
+    tok_k = (n >> 2) + 4 * (n & 3);
+  }
+};
+
+// Softmax state of one wave for one item: running max of head n (base 2),
+// this lane's share of head n's sum (tokens g + 4e), P.V accumulators
+// (rows = heads 4g..4g+3, column n = dim EPL*n + jj).
+template <int D>
+struct MfmaState {
+  float m, lsum;
+  f32x4 o[D / 16];
+  __device__ __forceinline__ void reset() {
+    m = -INFINITY;
+    lsum = 0.f;
+#pragma unroll
+    for (int jj = 0; jj < D / 16; ++jj) o[jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+};
+
+// Descriptors of the tile of pool block `bid` for KV head kvh; empty when
+// !ok (loads through them return zeros without touching memory).
+template <int DT, int D>
+__device__ __forceinline__ void tile_rsrc(const DecodeArgs& a, int bid, int kvh, bool ok, Rsrc& rk,
+                                          Rsrc& rv) {
+  using S = MfmaShape<DT, D>;
+  ok = ok && (uint32_t)bid < (uint32_t)a.num_blocks_i32;
+  const int64_t off = ((int64_t)(ok ? bid : 0) * a.num_kv_heads + kvh) * S::TILE_BYTES;
+  rk = make_rsrc(static_cast<const char*>(a.k_cache) + off, ok ? S::TILE_BYTES : 0);
+  rv = make_rsrc(static_cast<const char*>(a.v_cache) + off, ok ? S::TILE_BYTES : 0);
+}
+
+// The lane's share of one tile.  K: load jj is the tile's jj-th contiguous
+// KiB (lane l takes its 16-byte chunk l), so every load reads whole cache
+// lines; the rows reach the matrix-core layout through LDS (stage_k).  V:
+// rows g + 4e, already in the P.V operand layout.
+template <int DT, int D, bool SH>
+__device__ __forceinline__ void load_tile(Rsrc rk, Rsrc rv, const MfmaLane& ln,
+                                          u32x4 (&kr)[D / 32],
+                                          typename MfmaShape<DT, D>::VT (&vr)[4]) {
+  using S = MfmaShape<DT, D>;
+  const int lane = ln.n + 16 * ln.g;
+#pragma unroll
+  for (int jj = 0; jj < S::NJ; ++jj) kr[jj] = buf_load16<SH>(rk, (jj * 64 + lane) * 16);
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    vr[e] = S::VS::template load<SH>(rv, ((ln.g + 4 * e) * 16 + ln.n) *
+                                             (int)sizeof(typename S::VT));
+}
+
+// Force the wait for registers just loaded (an empty asm reading them).
+template <int N>
+__device__ __forceinline__ void wait_loaded(const u32x4 (&x)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) asm volatile("" ::"v"(x[i]));
+}
+
+// 16-byte slot of K chunk c of token row r in a wave's LDS staging tile.
+// Rows are padded by one chunk: both the row-wise writes and the
+// column-wise reads of the S operand then spread over the LDS banks, and
+// every load/store of one lane differs from its others by a constant offset.
+template <int D>
+__device__ __forceinline__ int kslot(int r, int c) {
+  return r * (D / 8 + 1) + c;
+}
+template <int D>
+constexpr int kKStageSlots = kBlockSize * (D / 8 + 1);
+
+// K tile (as loaded: load jj, lane l = chunk jj*64 + l of the tile) through
+// the wave's own LDS tile into the S operand layout, in place: lane (n, g) of
+// product jj gets chunk 4jj + g of token row tau(n).  Only this wave touches
+// `kst`, and its LDS accesses complete in order, so no barrier is needed.
+template <int D>
+__device__ __forceinline__ void stage_k(u32x4* kst, u32x4 (&kr)[D / 32], const MfmaLane& ln) {
+  constexpr int CPR = D / 8, NJ = D / 32;
+  const int lane = ln.n + 16 * ln.g;
+#pragma unroll
+  for (int jj = 0; jj < NJ; ++jj) {
+    const int idx = jj * 64 + lane;
+    kst[kslot<D>(idx / CPR, idx % CPR)] = kr[jj];
+  }
+#pragma unroll
+  for (int jj = 0; jj < NJ; ++jj) kr[jj] = kst[kslot<D>(ln.tok_k, 4 * jj + ln.g)];
+}
+
+// Fold one tile (`limit` of its 16 tokens in the context) into the state.
+template <int DT, int D, bool MASKED>
+__device__ __forceinline__ void consume_tile(MfmaState<D>& st, const u32x4 (&qb)[D / 32],
+                                             u32x4 (&kr)[D / 32],
+                                             typename MfmaShape<DT, D>::VT (&vr)[4], int limit,
+                                             float scale_log2, const MfmaLane& ln, u32x4* kst) {
+  using S = MfmaShape<DT, D>;
+  using VT = typename S::VT;
+  stage_k<D>(kst, kr, ln);
+  f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int jj = 0; jj < S::NJ; ++jj) sacc = mfma_qk<DT>(kr[jj], qb[jj], sacc);
+  float sc[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    sc[e] = sacc[e] * scale_log2;
+    if constexpr (MASKED) {
+      const bool ok = ln.g + 4 * e < limit;
+      sc[e] = ok ? sc[e] : -INFINITY;
+      if (!ok) vr[e] = VT{};  // whatever the slot holds must not reach P.V
+    }
+  }
+  float mb = __builtin_fmaxf(__builtin_fmaxf(sc[0], sc[1]), __builtin_fmaxf(sc[2], sc[3]));
+  mb = xor16_combine(mb, MaxOp{});
+  mb = xor32_combine(mb, MaxOp{});
+  // The running max moves only when a score passes it by more than
+  // kRescaleSlack: until then the tile's weights are taken against the older
+  // max (each below 2^kRescaleSlack) and the accumulators keep their scale.
+  // Numerator and denominator share that max, so the result is unchanged.
+  if (__builtin_amdgcn_ballot_w64(mb > st.m + kRescaleSlack) != 0) {  // wave-uniform
+    const float mn = __builtin_fmaxf(st.m, mb);
+    const float alpha = mn == -INFINITY ? 1.f : fast_exp2(st.m - mn);
+    st.lsum *= alpha;
+    st.m = mn;
+    // output rows 4g .. 4g+3 are heads 4g+e: fetch their factors
+    float arow[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      arow[e] = u2f((uint32_t)__builtin_amdgcn_ds_bpermute((4 * ln.g + e) << 2, (int)f2u(alpha)));
+#pragma unroll
+    for (int jj = 0; jj < S::EPL; ++jj)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) st.o[jj][e] *= arow[e];
+  }
+  float p[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) p[e] = fast_exp2(sc[e] - st.m);
+  if constexpr (MASKED) {
+    if (st.m == -INFINITY) {  // no valid token of this head so far
+#pragma unroll
+      for (int e = 0; e < 4; ++e) p[e] = 0.f;
+    }
+  }
+  st.lsum += (p[0] + p[1]) + (p[2] + p[3]);
+  const u32x2 pa{pack2<DT>(p[0], p[1]), pack2<DT>(p[2], p[3])};
+#pragma unroll
+  for (int jj = 0; jj < S::EPL; ++jj) {
+    const u32x2 vb{S::VS::half(vr[0], jj) | (S::VS::half(vr[1], jj) << 16),
+                   S::VS::half(vr[2], jj) | (S::VS::half(vr[3], jj) << 16)};
+    st.o[jj] = mfma_pv<DT>(pa, vb, st.o[jj]);
+  }
+}
+
+template <int DT, int D>
+__device__ __forceinline__ void consume_any(MfmaState<D>& st, const u32x4 (&qb)[D / 32],
+                                            u32x4 (&kr)[D / 32],
+                                            typename MfmaShape<DT, D>::VT (&vr)[4], int limit,
+                                            float scale_log2, const MfmaLane& ln, u32x4* kst) {
+  if (limit == kBlockSize)
+    consume_tile<DT, D, false>(st, qb, kr, vr, limit, scale_log2, ln, kst);
+  else
+    consume_tile<DT, D, true>(st, qb, kr, vr, limit, scale_log2, ln, kst);
+}
+
+}  // namespace pa

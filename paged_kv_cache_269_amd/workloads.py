@@ -46,7 +46,9 @@ _NAN_BITS = {"f16": 0x7E00, "bf16": 0x7FC0}
 # ``partition_size`` is the launch configuration the benchmark times: 0 (one
 # pass per sequence) where that measured fastest, 512-token partitions with
 # the log-sum-exp reduce for the long-context workload, whose definition
-# fixes them.
+# fixes them.  ``cascade`` marks the workload whose batch shares prompt pages:
+# it is decoded through the cascade entry point, which attends each run's
+# shared pages once.
 CONFIGS: Dict[str, dict] = {
     "tiny": dict(dtype="f32", num_seqs=4, num_q_heads=4, num_kv_heads=4, head_dim=64,
                  len_dist="fixed", lens=[1, 17, 33, 50], pool_blocks=32,
@@ -59,7 +61,7 @@ CONFIGS: Dict[str, dict] = {
                 partition_size=0, seed=3),
     "shared_prefix": dict(dtype="bf16", num_seqs=256, num_q_heads=32, num_kv_heads=32,
                           head_dim=128, len_dist="uniform", len_lo=64, len_hi=512,
-                          shared_prefix_blocks=64, partition_size=0, seed=4),
+                          shared_prefix_blocks=64, partition_size=0, cascade=True, seed=4),
     "long_context": dict(dtype="bf16", num_seqs=8, num_q_heads=64, num_kv_heads=8,
                          head_dim=128, len_dist="uniform", len_lo=32768, len_hi=131072,
                          partition_size=512, seed=5),

@@ -83,6 +83,33 @@ def test_workspace_bytes(hiplib):
 
 
 
+def _cascade(lib, **kw):
+    a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, cl=FAKE, B=2, Hq=8, Hkv=2, D=128, bs=16,
+             M=4, N=10, scale=0.1, dtype=1, maxlen=64, ws=FAKE, wsb=1 << 20, stream=None)
+    a.update(kw)
+    return lib.pa_paged_attention_decode_cascade(a["out"], a["q"], a["k"], a["v"], a["bt"],
+                                                 a["cl"], a["B"], a["Hq"], a["Hkv"], a["D"],
+                                                 a["bs"], a["M"], a["N"], a["scale"], a["dtype"],
+                                                 a["maxlen"], a["ws"], a["wsb"], a["stream"])
+
+
+def test_cascade_argument_checks_and_workspace(hiplib):
+    lib = hiplib.load_library()
+    f = lib.pa_cascade_workspace_bytes
+    rows = 5 * 8
+    al = lambda x: -(-x // 256) * 256
+    assert f(5, 8, 128) == al(5 * 4) + 2 * al(rows * 4) + al(rows * 128 * 4)
+    assert f(-1, 8, 128) == 0 and f(5, 0, 128) == 0
+    assert _cascade(lib, out=None) == NULL
+    assert _cascade(lib, D=96) == UNSUP
+    assert _cascade(lib, dtype=9) == UNSUP
+    assert _cascade(lib, Hq=6, Hkv=4) == SHAPE
+    assert _cascade(lib, ws=None, wsb=0) == WS
+    need = f(2, 8, 128)
+    assert _cascade(lib, wsb=need - 1) == WS
+    assert _cascade(lib, B=0, out=None, ws=None, wsb=0) == OK
+
+
 def test_reshape_and_reduce_argument_checks(hiplib):
     lib = hiplib.load_library()
     r = lib.pa_reshape_and_cache
