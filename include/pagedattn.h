@@ -69,7 +69,8 @@ enum pa_status {
   PA_ERR_WORKSPACE = 4,   /* workspace missing or smaller than pa_decode_workspace_bytes
                              (pa_cascade_workspace_bytes for the cascade entry point) */
   PA_ERR_RANGE = 5,       /* host table check: an entry, length or slot out of range */
-  PA_ERR_LAUNCH = 6       /* the HIP runtime refused a launch */
+  PA_ERR_LAUNCH = 6,      /* the HIP runtime refused a launch */
+  PA_ERR_EXHAUSTED = 7    /* block manager (pagedattn_blocks.h): no free block left */
 };
 
 /*

@@ -7,6 +7,8 @@ kernels.  Importing the package never loads the library; the first call does,
 and raises if the library is missing -- there is no fallback path.
 """
 from ._binding import (  # noqa: F401
+    BlockManager,
+    KVCacheExhausted,
     PagedAttnError,
     cascade_workspace,
     cascade_workspace_bytes,
@@ -26,7 +28,7 @@ from ._binding import (  # noqa: F401
 )
 
 __all__ = [
-    "PagedAttnError", "cascade_workspace", "cascade_workspace_bytes", "decode_workspace",
+    "BlockManager", "KVCacheExhausted", "PagedAttnError", "cascade_workspace", "cascade_workspace_bytes", "decode_workspace",
     "decode_workspace_bytes", "lib_path", "load_library", "paged_attention_decode",
     "paged_attention_decode_cascade", "paged_attention_reduce", "reshape_and_cache",
     "status_string", "validate_slots_host", "validate_tables_host", "version", "EXPORTS",

@@ -18,7 +18,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.environ.get("PAGEDATTN_LIB") or os.path.join(_HERE, "libpagedattn.so")
 
 PA_OK, PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_UNSUPPORTED = 0, 1, 2, 3
-PA_ERR_WORKSPACE, PA_ERR_RANGE, PA_ERR_LAUNCH = 4, 5, 6
+PA_ERR_WORKSPACE, PA_ERR_RANGE, PA_ERR_LAUNCH, PA_ERR_EXHAUSTED = 4, 5, 6, 7
 
 # Every symbol the header declares, with its ctypes signature.
 _P, _I32, _I64, _F32, _SZ = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
@@ -40,6 +40,18 @@ EXPORTS = {
     "pa_validate_slots_host": (ctypes.c_int, [_P, _I32, _I64, _I32]),
     "pa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "pa_version": (ctypes.c_char_p, []),
+    # host block manager (include/pagedattn_blocks.h)
+    "pa_bm_create": (ctypes.c_void_p, [_I64, _I32]),
+    "pa_bm_destroy": (None, [_P]),
+    "pa_bm_allocate": (ctypes.c_int, [_P, _I64, _I64]),
+    "pa_bm_share": (ctypes.c_int, [_P, _I64, _I64, _I64]),
+    "pa_bm_append": (ctypes.c_int, [_P, _I64, ctypes.POINTER(ctypes.c_int64)]),
+    "pa_bm_append_batch": (ctypes.c_int, [_P, _P, _I32, _P]),
+    "pa_bm_free": (ctypes.c_int, [_P, _I64]),
+    "pa_bm_num_free": (ctypes.c_int64, [_P]),
+    "pa_bm_seq_len": (ctypes.c_int64, [_P, _I64]),
+    "pa_bm_block_tables": (ctypes.c_int, [_P, _P, _I32, _I32, _I32, _P, _P]),
+    "pa_bm_free_blocks": (ctypes.c_int, [_P, _P, _I64]),
 }
 
 
@@ -242,3 +254,86 @@ def validate_slots_host(slot_mapping, num_blocks: int, block_size: int = 16) -> 
     sm = np.ascontiguousarray(slot_mapping, dtype=np.int64)
     return int(load_library().pa_validate_slots_host(
         sm.ctypes.data_as(ctypes.c_void_p), sm.shape[0], int(num_blocks), block_size))
+
+
+class KVCacheExhausted(PagedAttnError):
+    """No free block left in a BlockManager."""
+
+
+class BlockManager:
+    """The library's host block manager (pagedattn_blocks.h): free-block
+    deque, ceil-div allocation, reference-counted sharing, one more block
+    when a request grows past its last one.  Host memory only."""
+
+    def __init__(self, num_blocks: int, block_size: int = 16):
+        self._lib = load_library()
+        self._h = self._lib.pa_bm_create(int(num_blocks), int(block_size))
+        if not self._h:
+            raise ValueError("invalid block manager sizes (or out of host memory)")
+        self.num_blocks, self.block_size = int(num_blocks), int(block_size)
+
+    def close(self) -> None:
+        if getattr(self, "_h", None):
+            self._lib.pa_bm_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        self.close()
+
+    def _rc(self, fn: str, rc: int) -> None:
+        if rc == PA_ERR_EXHAUSTED:
+            raise KVCacheExhausted(fn, rc)
+        _check(fn, rc)
+
+    def allocate(self, request_id: int, num_tokens: int) -> None:
+        self._rc("pa_bm_allocate", self._lib.pa_bm_allocate(self._h, request_id, num_tokens))
+
+    def share(self, src_id: int, dst_id: int, num_blocks: int) -> None:
+        self._rc("pa_bm_share", self._lib.pa_bm_share(self._h, src_id, dst_id, num_blocks))
+
+    def append(self, request_id: int) -> int:
+        slot = ctypes.c_int64(-1)
+        self._rc("pa_bm_append", self._lib.pa_bm_append(self._h, request_id, ctypes.byref(slot)))
+        return slot.value
+
+    def append_batch(self, request_ids, slots=None):
+        """One token for each request (distinct ids); returns the slots
+        (numpy int64, written into ``slots`` when given)."""
+        import numpy as np
+        ids = np.ascontiguousarray(request_ids, dtype=np.int64)
+        if slots is None:
+            slots = np.empty(ids.shape[0], np.int64)
+        if slots.dtype != np.int64 or not slots.flags.c_contiguous or slots.shape[0] < ids.shape[0]:
+            raise ValueError("slots must be a contiguous int64 array of at least len(request_ids)")
+        self._rc("pa_bm_append_batch", self._lib.pa_bm_append_batch(
+            self._h, ids.ctypes.data_as(ctypes.c_void_p), ids.shape[0],
+            slots.ctypes.data_as(ctypes.c_void_p)))
+        return slots
+
+    def free(self, request_id: int) -> None:
+        self._rc("pa_bm_free", self._lib.pa_bm_free(self._h, request_id))
+
+    def num_free(self) -> int:
+        return int(self._lib.pa_bm_num_free(self._h))
+
+    def seq_len(self, request_id: int) -> int:
+        return int(self._lib.pa_bm_seq_len(self._h, request_id))
+
+    def block_tables(self, request_ids, max_blocks_per_seq: int, pad: int = 0):
+        """(block_tables [n, max_blocks] int32, context_lens [n] int32) as numpy."""
+        import numpy as np
+        ids = np.ascontiguousarray(request_ids, dtype=np.int64)
+        bt = np.empty((ids.shape[0], max_blocks_per_seq), np.int32)
+        cl = np.empty(ids.shape[0], np.int32)
+        self._rc("pa_bm_block_tables", self._lib.pa_bm_block_tables(
+            self._h, ids.ctypes.data_as(ctypes.c_void_p), ids.shape[0], max_blocks_per_seq, pad,
+            bt.ctypes.data_as(ctypes.c_void_p), cl.ctypes.data_as(ctypes.c_void_p)))
+        return bt, cl
+
+    def free_blocks(self):
+        """The free deque, front first (numpy int32)."""
+        import numpy as np
+        out = np.empty(max(self.num_free(), 1), np.int32)
+        self._rc("pa_bm_free_blocks", self._lib.pa_bm_free_blocks(
+            self._h, out.ctypes.data_as(ctypes.c_void_p), out.shape[0]))
+        return out[:self.num_free()]

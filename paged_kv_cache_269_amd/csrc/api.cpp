@@ -191,6 +191,7 @@ const char* pa_status_string(int status) {
     case PA_ERR_WORKSPACE: return "workspace missing or too small";
     case PA_ERR_RANGE: return "table entry, context length or slot out of range";
     case PA_ERR_LAUNCH: return "the HIP runtime refused a kernel launch";
+    case PA_ERR_EXHAUSTED: return "KV cache exhausted: no free block left";
     default: return "unknown status";
   }
 }

@@ -10,16 +10,19 @@ import pytest
 import oracle
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "pagedattn.h")
+INCLUDE = os.path.join(ROOT, "include")
+HEADERS = [os.path.join(INCLUDE, f) for f in sorted(os.listdir(INCLUDE)) if f.endswith(".h")]
 
 OK, NULL, SHAPE, UNSUP, WS, RANGE = 0, 1, 2, 3, 4, 5
 FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation first
 
 
 def declared_symbols():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(pa_\w+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(pa_\w+)\s*\(", text))
+    return sorted(names)
 
 
 def test_library_exports_every_declared_symbol(hiplib):
@@ -33,7 +36,7 @@ def test_library_exports_every_declared_symbol(hiplib):
 
 def test_version_and_status_strings(hiplib):
     assert "gfx950" in hiplib.version()
-    for code in range(0, 7):
+    for code in range(0, 8):
         assert hiplib.status_string(code) and hiplib.status_string(code) != "unknown status"
     assert hiplib.status_string(99) == "unknown status"
 
