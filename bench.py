@@ -48,6 +48,9 @@ def parse_args(argv=None):
                     help="copies of the KV pool used in turn by consecutive steps, so that no "
                          "step finds its K/V in the 256 MB Infinity Cache from the step "
                          "before (1 = re-read the same pool every step)")
+    ap.add_argument("--loop-steps", type=int, default=0,
+                    help="also time this many steps of a multi-step decode loop driven by the "
+                         "host block manager (one new token per sequence per step)")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB before warmup, as the "
                          "known-size reference for HBM byte counters")
@@ -116,6 +119,121 @@ def cpu_baseline(w, target_s: float):
             "seqs_per_s": round(n / dt, 3), "seconds": round(dt, 3),
             "sample": f"first {n} of {w.num_seqs} sequences, all {Hq} query heads, "
                       f"float64 C oracle with OpenMP, median of {reps} run(s)"}
+
+
+def decode_loop(args, w, dev):
+    """Multi-step decode through the library's host block manager: each step
+    appends one token to every sequence (the manager hands out the slots and
+    takes a new block at each 16-token boundary) and exports the block tables
+    and lengths into a pinned host buffer; the device part -- one copy of that
+    buffer, the KV write and the decode -- is a captured HIP graph, replayed
+    once per step.  Two buffer/graph sets alternate so that the host fills one
+    while the device reads the other.  The workload's context lengths are the
+    prompts; their K/V is whatever the freshly allocated pool holds (timing
+    only; the multi-step GPU test checks results)."""
+    import numpy as np
+    import torch
+    import paged_kv_cache_269_amd as pa
+    from paged_kv_cache_269_amd import workloads as W
+
+    S, Wm = args.loop_steps, 8
+    B, Hq, Hkv, D = w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim
+    lens = w.context_lens.astype(np.int64)
+    final = lens + S + Wm
+    N = int(((final + 15) // 16).sum() * 1.05) + 16
+    M = int((final.max() + 15) // 16)
+    maxlen = int(final.max())
+    tdt = W.torch_dtype(w.dtype)
+    gen = torch.Generator(device=dev).manual_seed(7)
+    kc = torch.randn((N, Hkv, 16, D), generator=gen, device=dev).to(tdt)
+    vc = torch.randn((N, Hkv, 16, D), generator=gen, device=dev).to(tdt)
+    q = torch.randn((B, Hq, D), generator=gen, device=dev).to(tdt)
+    knew = torch.randn((B, Hkv, D), generator=gen, device=dev).to(tdt)
+    vnew = torch.randn((B, Hkv, D), generator=gen, device=dev).to(tdt)
+    out = torch.empty_like(q)
+    ws = pa.decode_workspace(B, Hq, D, maxlen, w.partition_size, device=dev)
+    bm = pa.BlockManager(N, 16)
+    ids = np.arange(B, dtype=np.int64)
+    for s in range(B):
+        bm.allocate(s, int(lens[s]))
+    # one packed int32 buffer per set: [slots (B int64) | tables (B x M) | lens (B)]
+    n32 = 2 * B + B * M + B
+    sets = []
+    for _ in range(2):
+        h = torch.empty(n32, dtype=torch.int32).pin_memory()
+        dvb = torch.empty(n32, dtype=torch.int32, device=dev)
+        hn = h.numpy()
+        sets.append(dict(
+            h=h, d=dvb,
+            slots=hn[:2 * B].view(np.int64), bt=hn[2 * B:2 * B + B * M].reshape(B, M),
+            cl=hn[2 * B + B * M:],
+            d_slots=dvb[:2 * B].view(torch.int64), d_bt=dvb[2 * B:2 * B + B * M].view(B, M),
+            d_cl=dvb[2 * B + B * M:], done=None))
+
+    def device_part(st, stream):
+        st["d"].copy_(st["h"], non_blocking=True)
+        pa.reshape_and_cache(knew, vnew, kc, vc, st["d_slots"], stream=stream)
+        pa.paged_attention_decode(out, q, kc, vc, st["d_bt"], st["d_cl"], w.scale, maxlen,
+                                  partition_size=w.partition_size, workspace=ws, stream=stream)
+
+    # fill both sets once (valid tables) and capture one graph per set
+    for st in sets:
+        bm.block_tables(ids, M, 0, out=(st["bt"], st["cl"]))
+        st["slots"][:] = -1                     # no KV write during capture warm-up
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for st in sets:
+            device_part(st, side)               # eager warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for st in sets:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            device_part(st, torch.cuda.current_stream())
+        st["graph"] = g
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        st = sets[i % 2]
+        if st["done"] is not None:
+            st["done"].synchronize()            # the previous copy out of this buffer has run
+        bm.append_batch(ids, st["slots"])
+        bm.block_tables(ids, M, 0, out=(st["bt"], st["cl"]))
+        st["graph"].replay()
+        if st["done"] is None:
+            st["done"] = torch.cuda.Event()
+        st["done"].record(stream)
+
+    for i in range(Wm):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    host_s = 0.0
+    for i in range(Wm, Wm + S):
+        h0 = time.perf_counter()
+        step(i)
+        host_s += time.perf_counter() - h0
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    # the device part alone, replayed back to back
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(20):
+        sets[i % 2]["graph"].replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    dev_us = e0.elapsed_time(e1) * 1e3 / 20
+    bm.close()
+    return {"steps": S, "sequences": B, "ms_per_step": round(wall * 1e3 / S, 4),
+            "tokens_per_s": round(B * S / wall, 1),
+            "host_ms_per_step": round(host_s * 1e3 / S, 4),
+            "device_graph_us_per_step": round(dev_us, 2),
+            "pool_blocks": N,
+            "note": "per step: block-manager appends + table export on the host, then one HIP "
+                    "graph (packed H2D copy, reshape_and_cache, decode)"}
 
 
 def main(argv=None) -> int:
@@ -246,6 +364,10 @@ def main(argv=None) -> int:
                      "launch_us_p90": round(float(np.percentile(dec_ms, 90)) * 1e3, 2),
                      "algorithmic_bytes_per_launch": ab["total"]},
     }
+    if args.loop_steps > 0:
+        del pools, d, ws
+        torch.cuda.empty_cache()
+        result["decode_loop"] = decode_loop(args, w, dev)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(result), flush=True)

@@ -319,12 +319,19 @@ class BlockManager:
     def seq_len(self, request_id: int) -> int:
         return int(self._lib.pa_bm_seq_len(self._h, request_id))
 
-    def block_tables(self, request_ids, max_blocks_per_seq: int, pad: int = 0):
-        """(block_tables [n, max_blocks] int32, context_lens [n] int32) as numpy."""
+    def block_tables(self, request_ids, max_blocks_per_seq: int, pad: int = 0, out=None):
+        """(block_tables [n, max_blocks] int32, context_lens [n] int32) as numpy
+        (written into ``out`` = (tables, lens) when given)."""
         import numpy as np
         ids = np.ascontiguousarray(request_ids, dtype=np.int64)
-        bt = np.empty((ids.shape[0], max_blocks_per_seq), np.int32)
-        cl = np.empty(ids.shape[0], np.int32)
+        if out is None:
+            bt = np.empty((ids.shape[0], max_blocks_per_seq), np.int32)
+            cl = np.empty(ids.shape[0], np.int32)
+        else:
+            bt, cl = out
+            if (bt.dtype != np.int32 or cl.dtype != np.int32 or not bt.flags.c_contiguous
+                    or bt.shape != (ids.shape[0], max_blocks_per_seq) or cl.shape != ids.shape):
+                raise ValueError("out must be int32 arrays [n, max_blocks] and [n]")
         self._rc("pa_bm_block_tables", self._lib.pa_bm_block_tables(
             self._h, ids.ctypes.data_as(ctypes.c_void_p), ids.shape[0], max_blocks_per_seq, pad,
             bt.ctypes.data_as(ctypes.c_void_p), cl.ctypes.data_as(ctypes.c_void_p)))
