@@ -188,6 +188,40 @@ int pa_paged_attention_decode_cascade(void* out, const void* q, const void* k_ca
 size_t pa_cascade_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim);
 
 /*
+ * Copy-on-write of shared blocks ([CX] §2.1: requests of one prompt --
+ * parallel sampling, beam search -- share its pages; [DM] sharing
+ * mechanism): for every pair i, block block_pairs[2i] of both caches (all
+ * KV heads) is copied onto block block_pairs[2i+1].  block_pairs is a
+ * device array [num_pairs, 2] int32.  Destinations must be distinct and no
+ * destination may be a source in the same call (a caller error otherwise;
+ * pa_validate_copy_host checks a host copy); pairs naming a block outside
+ * [0, num_blocks) are skipped.  num_pairs <= 65535; 0 is a no-op.
+ */
+int pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_pairs, int32_t num_pairs,
+                   int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                   int64_t num_blocks, int32_t dtype, void* stream);
+
+/*
+ * Swap blocks between two caches of the same layout, one of them usually in
+ * pinned host memory ([DM] block manager: blocks swapped out to CPU memory
+ * and back in): for every pair i, block_bytes bytes at block
+ * block_pairs[2i] of src_cache go to block block_pairs[2i+1] of dst_cache
+ * (one call per cache: K and V are separate arrays).  block_pairs is a host
+ * array [num_pairs, 2] int64; runs of consecutive pairs move as one copy.
+ * Enqueued on `stream` as asynchronous copies (host memory must be pinned
+ * for them to be asynchronous).  Negative ids give PA_ERR_RANGE (nothing
+ * enqueued); the caller keeps ids inside both caches.
+ */
+int pa_swap_blocks(const void* src_cache, void* dst_cache, const int64_t* block_pairs,
+                   int32_t num_pairs, int64_t block_bytes, void* stream);
+
+/*
+ * Host check of copy pairs (host pointer): ids in [0, num_blocks), distinct
+ * destinations, no destination used as a source.  PA_OK or PA_ERR_RANGE.
+ */
+int pa_validate_copy_host(const int32_t* block_pairs, int32_t num_pairs, int64_t num_blocks);
+
+/*
  * Host-side check of block tables (host pointers): every entry a sequence
  * uses, logical blocks 0 .. ceil(L/block_size)-1, must lie in
  * [0, num_blocks), ceil(L/block_size) must not exceed max_blocks_per_seq and

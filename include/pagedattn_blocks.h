@@ -49,18 +49,30 @@ int pa_bm_allocate(pa_block_manager* m, int64_t request_id, int64_t num_tokens);
  * unknown source, an existing destination or too many blocks. */
 int pa_bm_share(pa_block_manager* m, int64_t src_id, int64_t dst_id, int64_t num_blocks);
 
-/* Add one token to a request: when its length is a multiple of block_size a
- * block is taken from the front first.  *slot receives the new token's slot
- * (for pa_reshape_and_cache).  PA_ERR_EXHAUSTED (length unchanged) when no
- * block is free; PA_ERR_RANGE for an unknown id. */
-int pa_bm_append(pa_block_manager* m, int64_t request_id, int64_t* slot);
+/* New request dst_id maps every block of src_id (one more reference each)
+ * and has its length: two continuations of one prompt (parallel sampling,
+ * beam search).  PA_ERR_RANGE for an unknown source or existing
+ * destination. */
+int pa_bm_fork(pa_block_manager* m, int64_t src_id, int64_t dst_id);
 
-/* pa_bm_append for each of n distinct requests, slots[i] for request_ids[i]
- * (host arrays).  All or nothing: PA_ERR_RANGE for an unknown or repeated
- * id, PA_ERR_EXHAUSTED when the requests at a block boundary need more
- * blocks than are free -- in both cases no request changes. */
+/* Add one token to a request.  When its length is a multiple of block_size a
+ * block is taken from the front first; when the token would land in a last
+ * block that other requests still map, the request gets a fresh block from
+ * the front in its place (copy-on-write): copy_pair receives (shared block,
+ * fresh block), which the caller copies with pa_copy_blocks before writing
+ * the token, else (-1, -1).  *slot receives the new token's slot (for
+ * pa_reshape_and_cache).  PA_ERR_EXHAUSTED (nothing changed) when no block is
+ * free; PA_ERR_RANGE for an unknown id. */
+int pa_bm_append(pa_block_manager* m, int64_t request_id, int64_t* slot, int32_t* copy_pair);
+
+/* pa_bm_append for each of n distinct requests in order, slots[i] for
+ * request_ids[i] (host arrays); the copies it needs go to copy_pairs
+ * ([n, 2] capacity, the first *num_copies filled), ready for
+ * pa_copy_blocks.  All or nothing: PA_ERR_RANGE for an unknown or repeated
+ * id, PA_ERR_EXHAUSTED when the batch needs more blocks than are free -- in
+ * both cases no request changes. */
 int pa_bm_append_batch(pa_block_manager* m, const int64_t* request_ids, int32_t n,
-                       int64_t* slots);
+                       int64_t* slots, int32_t* copy_pairs, int32_t* num_copies);
 
 /* Drop a request: one reference less on each of its blocks, blocks whose
  * count reaches 0 go to the back of the free deque in the request's block

@@ -18,11 +18,15 @@ Readings where the printed code is silent or would lose state:
   * allocating an id that already holds blocks is an error;
   * sharing hands the first k whole blocks of one request to a new request
     (its length becomes k * block_size), one more reference each;
+  * forking hands every block of a request to a new one (same length;
+    "vLLM 2026 推理引擎全解" (chenxutan.com) §2.1: parallel sampling and beam
+    search share a prompt's pages), one more reference each;
   * appending one token to a request whose length is a multiple of the
-    block size takes a new block first; the token's slot is
-    block_table[(L-1) // bs] * bs + (L-1) % bs for the new length L
-    ("vLLM 2026 推理引擎全解" (chenxutan.com) §2.2: page_id * BLOCK_SIZE +
-    page_offset).
+    block size takes a new block first; a token that would land in a last
+    block other requests still map gets a fresh block in its place, whose
+    contents the caller copies from the shared one (copy-on-write); the
+    token's slot is block_table[(L-1) // bs] * bs + (L-1) % bs for the new
+    length L (same page, §2.2: page_id * BLOCK_SIZE + page_offset).
 """
 from __future__ import annotations
 
@@ -75,16 +79,33 @@ class BlockManager:
         self.tables[dst] = list(blocks)
         self.lengths[dst] = num_blocks * self.block_size
 
-    def append(self, rid: int) -> int:
+    def fork(self, src: int, dst: int) -> None:
+        if src not in self.tables or dst in self.tables:
+            raise ValueError("bad request ids")
+        for b in self.tables[src]:
+            self.refcount[b] += 1
+        self.tables[dst] = list(self.tables[src])
+        self.lengths[dst] = self.lengths[src]
+
+    def append(self, rid: int):
+        """One more token: returns (slot, copy) with copy = (shared block,
+        fresh block) when the request had to leave a shared block, else None."""
         if rid not in self.tables:
             raise ValueError("unknown request")
         L = self.lengths[rid]
+        tab = self.tables[rid]
+        copy = None
         if L % self.block_size == 0:
-            self.tables[rid] += self._take(1)
+            tab += self._take(1)
+        elif self.refcount[tab[-1]] > 1:
+            fresh = self._take(1)[0]
+            self.refcount[tab[-1]] -= 1
+            copy = (tab[-1], fresh)
+            tab[-1] = fresh
         L += 1
         self.lengths[rid] = L
         t = L - 1
-        return self.tables[rid][t // self.block_size] * self.block_size + t % self.block_size
+        return tab[t // self.block_size] * self.block_size + t % self.block_size, copy
 
     def free(self, rid: int) -> None:
         if rid not in self.tables:
@@ -100,3 +121,15 @@ class BlockManager:
 
     def num_free(self) -> int:
         return len(self.free_blocks)
+
+
+def copy_blocks(k_cache, v_cache, pairs) -> None:
+    """Block copy of the copy-on-write step, on host arrays [N, Hkv, bs, D]:
+    every (src, dst) pair gets block src of both caches written onto block
+    dst (sources read before any destination is written)."""
+    pairs = [(int(a), int(b)) for a, b in pairs]
+    ks = [k_cache[a].copy() for a, _ in pairs]
+    vs = [v_cache[a].copy() for a, _ in pairs]
+    for (_, b), kb, vb in zip(pairs, ks, vs):
+        k_cache[b] = kb
+        v_cache[b] = vb

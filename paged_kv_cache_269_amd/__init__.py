@@ -12,6 +12,7 @@ from ._binding import (  # noqa: F401
     PagedAttnError,
     cascade_workspace,
     cascade_workspace_bytes,
+    copy_blocks,
     decode_workspace,
     decode_workspace_bytes,
     lib_path,
@@ -21,6 +22,8 @@ from ._binding import (  # noqa: F401
     paged_attention_reduce,
     reshape_and_cache,
     status_string,
+    swap_blocks,
+    validate_copy_host,
     validate_slots_host,
     validate_tables_host,
     version,
@@ -28,8 +31,9 @@ from ._binding import (  # noqa: F401
 )
 
 __all__ = [
-    "BlockManager", "KVCacheExhausted", "PagedAttnError", "cascade_workspace", "cascade_workspace_bytes", "decode_workspace",
-    "decode_workspace_bytes", "lib_path", "load_library", "paged_attention_decode",
-    "paged_attention_decode_cascade", "paged_attention_reduce", "reshape_and_cache",
-    "status_string", "validate_slots_host", "validate_tables_host", "version", "EXPORTS",
+    "BlockManager", "KVCacheExhausted", "PagedAttnError", "cascade_workspace",
+    "cascade_workspace_bytes", "copy_blocks", "decode_workspace", "decode_workspace_bytes",
+    "lib_path", "load_library", "paged_attention_decode", "paged_attention_decode_cascade",
+    "paged_attention_reduce", "reshape_and_cache", "status_string", "swap_blocks",
+    "validate_copy_host", "validate_slots_host", "validate_tables_host", "version", "EXPORTS",
 ]

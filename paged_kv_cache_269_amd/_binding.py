@@ -26,6 +26,9 @@ _P, _I32, _I64, _F32, _SZ = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ct
 EXPORTS = {
     "pa_reshape_and_cache": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I64,
                                             _I32, _P]),
+    "pa_copy_blocks": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _I32, _I32, _I64, _I32, _P]),
+    "pa_swap_blocks": (ctypes.c_int, [_P, _P, _P, _I32, _I64, _P]),
+    "pa_validate_copy_host": (ctypes.c_int, [_P, _I32, _I64]),
     "pa_paged_attention_decode": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32,
                                                  _I32, _I32, _I32, _I64, _F32, _I32, _I32,
                                                  _I32, _P, _SZ, _P]),
@@ -45,8 +48,9 @@ EXPORTS = {
     "pa_bm_destroy": (None, [_P]),
     "pa_bm_allocate": (ctypes.c_int, [_P, _I64, _I64]),
     "pa_bm_share": (ctypes.c_int, [_P, _I64, _I64, _I64]),
-    "pa_bm_append": (ctypes.c_int, [_P, _I64, ctypes.POINTER(ctypes.c_int64)]),
-    "pa_bm_append_batch": (ctypes.c_int, [_P, _P, _I32, _P]),
+    "pa_bm_fork": (ctypes.c_int, [_P, _I64, _I64]),
+    "pa_bm_append": (ctypes.c_int, [_P, _I64, ctypes.POINTER(ctypes.c_int64), _P]),
+    "pa_bm_append_batch": (ctypes.c_int, [_P, _P, _I32, _P, _P, _P]),
     "pa_bm_free": (ctypes.c_int, [_P, _I64]),
     "pa_bm_num_free": (ctypes.c_int64, [_P]),
     "pa_bm_seq_len": (ctypes.c_int64, [_P, _I64]),
@@ -239,6 +243,51 @@ def paged_attention_reduce(out, max_logits, exp_sums, tmp_out, context_lens,
     _check("pa_paged_attention_reduce", rc)
 
 
+def copy_blocks(k_cache, v_cache, block_pairs, stream=None) -> None:
+    """Copy block src onto block dst of both caches for every (src, dst) row
+    of ``block_pairs`` (device int32 [n, 2])."""
+    import torch
+    N, Hkv, bs, D = k_cache.shape
+    if v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype:
+        raise ValueError("k_cache and v_cache must match")
+    if block_pairs.dim() != 2 or block_pairs.shape[1] != 2:
+        raise ValueError("block_pairs must be [n, 2]")
+    n = block_pairs.shape[0]
+    rc = load_library().pa_copy_blocks(
+        _dev_ptr(k_cache, "k_cache"), _dev_ptr(v_cache, "v_cache"),
+        _dev_ptr(block_pairs, "block_pairs", torch.int32) if n else None, n, Hkv, D, bs, N,
+        _dtype_code(k_cache), _stream_handle(stream))
+    _check("pa_copy_blocks", rc)
+
+
+def swap_blocks(src_cache, dst_cache, block_pairs, stream=None) -> None:
+    """Copy block src of ``src_cache`` onto block dst of ``dst_cache`` for
+    every (src, dst) row of ``block_pairs`` (host int64 [n, 2]); one of the
+    caches is usually pinned host memory."""
+    import numpy as np
+    if src_cache.shape[1:] != dst_cache.shape[1:] or src_cache.dtype != dst_cache.dtype:
+        raise ValueError("caches must share a block layout and element type")
+    if not (src_cache.is_contiguous() and dst_cache.is_contiguous()):
+        raise ValueError("caches must be contiguous")
+    pairs = np.ascontiguousarray(block_pairs, dtype=np.int64).reshape(-1, 2)
+    if pairs.size and (pairs[:, 0].max() >= src_cache.shape[0] or
+                       pairs[:, 1].max() >= dst_cache.shape[0]):
+        raise ValueError("block id outside a cache")
+    block_bytes = src_cache[0].numel() * src_cache.element_size()
+    rc = load_library().pa_swap_blocks(
+        ctypes.c_void_p(src_cache.data_ptr()), ctypes.c_void_p(dst_cache.data_ptr()),
+        pairs.ctypes.data_as(ctypes.c_void_p), pairs.shape[0], block_bytes,
+        _stream_handle(stream))
+    _check("pa_swap_blocks", rc)
+
+
+def validate_copy_host(block_pairs, num_blocks: int) -> int:
+    import numpy as np
+    p = np.ascontiguousarray(block_pairs, dtype=np.int32).reshape(-1, 2)
+    return int(load_library().pa_validate_copy_host(p.ctypes.data_as(ctypes.c_void_p),
+                                                    p.shape[0], int(num_blocks)))
+
+
 def validate_tables_host(block_tables, context_lens, num_blocks: int, block_size: int = 16) -> int:
     """Host check of numpy int32 tables; returns the library status code."""
     import numpy as np
@@ -291,24 +340,41 @@ class BlockManager:
     def share(self, src_id: int, dst_id: int, num_blocks: int) -> None:
         self._rc("pa_bm_share", self._lib.pa_bm_share(self._h, src_id, dst_id, num_blocks))
 
-    def append(self, request_id: int) -> int:
-        slot = ctypes.c_int64(-1)
-        self._rc("pa_bm_append", self._lib.pa_bm_append(self._h, request_id, ctypes.byref(slot)))
-        return slot.value
+    def fork(self, src_id: int, dst_id: int) -> None:
+        self._rc("pa_bm_fork", self._lib.pa_bm_fork(self._h, src_id, dst_id))
 
-    def append_batch(self, request_ids, slots=None):
-        """One token for each request (distinct ids); returns the slots
-        (numpy int64, written into ``slots`` when given)."""
+    def append(self, request_id: int):
+        """One more token: (slot, copy) where copy = (shared block, fresh
+        block) to copy before writing the token, or None."""
+        import numpy as np
+        slot = ctypes.c_int64(-1)
+        pair = np.empty(2, np.int32)
+        self._rc("pa_bm_append", self._lib.pa_bm_append(
+            self._h, request_id, ctypes.byref(slot), pair.ctypes.data_as(ctypes.c_void_p)))
+        return slot.value, (None if pair[0] < 0 else (int(pair[0]), int(pair[1])))
+
+    def append_batch(self, request_ids, slots=None, copies=None):
+        """One token for each request (distinct ids), in order.  Returns
+        (slots, copy_pairs): the slots (numpy int64, written into ``slots``
+        when given) and the copy-on-write pairs [k, 2] int32 to hand to
+        copy_blocks first (a view of ``copies`` when given, [n, 2] int32)."""
         import numpy as np
         ids = np.ascontiguousarray(request_ids, dtype=np.int64)
+        n = ids.shape[0]
         if slots is None:
-            slots = np.empty(ids.shape[0], np.int64)
-        if slots.dtype != np.int64 or not slots.flags.c_contiguous or slots.shape[0] < ids.shape[0]:
+            slots = np.empty(n, np.int64)
+        if copies is None:
+            copies = np.empty((max(n, 1), 2), np.int32)
+        if slots.dtype != np.int64 or not slots.flags.c_contiguous or slots.shape[0] < n:
             raise ValueError("slots must be a contiguous int64 array of at least len(request_ids)")
+        if copies.dtype != np.int32 or not copies.flags.c_contiguous or copies.shape[0] < n:
+            raise ValueError("copies must be a contiguous int32 array [len(request_ids), 2]")
+        nc = ctypes.c_int32(0)
         self._rc("pa_bm_append_batch", self._lib.pa_bm_append_batch(
-            self._h, ids.ctypes.data_as(ctypes.c_void_p), ids.shape[0],
-            slots.ctypes.data_as(ctypes.c_void_p)))
-        return slots
+            self._h, ids.ctypes.data_as(ctypes.c_void_p), n,
+            slots.ctypes.data_as(ctypes.c_void_p), copies.ctypes.data_as(ctypes.c_void_p),
+            ctypes.byref(nc)))
+        return slots, copies[:nc.value]
 
     def free(self, request_id: int) -> None:
         self._rc("pa_bm_free", self._lib.pa_bm_free(self._h, request_id))

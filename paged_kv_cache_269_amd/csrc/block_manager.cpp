@@ -95,13 +95,45 @@ int pa_bm_share(pa_block_manager* m, int64_t src_id, int64_t dst_id, int64_t num
   return PA_OK;
 }
 
-int pa_bm_append(pa_block_manager* m, int64_t request_id, int64_t* slot) {
-  if (!m || !slot) return PA_ERR_NULL;
-  auto it = m->seqs.find(request_id);
-  if (it == m->seqs.end()) return PA_ERR_RANGE;
-  pa_block_manager::Seq& s = it->second;
+int pa_bm_fork(pa_block_manager* m, int64_t src_id, int64_t dst_id) {
+  if (!m) return PA_ERR_NULL;
+  auto it = m->seqs.find(src_id);
+  if (it == m->seqs.end() || m->seqs.count(dst_id)) return PA_ERR_RANGE;
   try {
-    if (s.len % m->block_size == 0 && !m->take(1, s.blocks)) return PA_ERR_EXHAUSTED;
+    pa_block_manager::Seq s = it->second;
+    for (int32_t b : s.blocks) ++m->refcount[b];
+    m->seqs.emplace(dst_id, std::move(s));
+  } catch (...) {
+    return PA_ERR_EXHAUSTED;
+  }
+  return PA_OK;
+}
+
+namespace {
+
+// Blocks one append to `s` takes: a new block at a block boundary, or a
+// private copy of a last block that other requests still map (`extra_refs`
+// of those references already given up earlier in the same batch).
+int blocks_needed(const pa_block_manager* m, const pa_block_manager::Seq& s, int extra_refs) {
+  if (s.len % m->block_size == 0) return 1;
+  return m->refcount[s.blocks.back()] - extra_refs > 1 ? 1 : 0;
+}
+
+int append_one(pa_block_manager* m, pa_block_manager::Seq& s, int64_t* slot, int32_t* copy_pair) {
+  copy_pair[0] = copy_pair[1] = -1;
+  try {
+    if (s.len % m->block_size == 0) {
+      if (!m->take(1, s.blocks)) return PA_ERR_EXHAUSTED;
+    } else if (m->refcount[s.blocks.back()] > 1) {
+      // copy-on-write: the token would land in a block other requests map
+      std::vector<int32_t> fresh;
+      if (!m->take(1, fresh)) return PA_ERR_EXHAUSTED;
+      const int32_t old = s.blocks.back();
+      --m->refcount[old];
+      s.blocks.back() = fresh[0];
+      copy_pair[0] = old;
+      copy_pair[1] = fresh[0];
+    }
   } catch (...) {
     return PA_ERR_EXHAUSTED;
   }
@@ -110,31 +142,56 @@ int pa_bm_append(pa_block_manager* m, int64_t request_id, int64_t* slot) {
   return PA_OK;
 }
 
+}  // namespace
+
+int pa_bm_append(pa_block_manager* m, int64_t request_id, int64_t* slot, int32_t* copy_pair) {
+  if (!m || !slot || !copy_pair) return PA_ERR_NULL;
+  auto it = m->seqs.find(request_id);
+  if (it == m->seqs.end()) return PA_ERR_RANGE;
+  return append_one(m, it->second, slot, copy_pair);
+}
+
 int pa_bm_append_batch(pa_block_manager* m, const int64_t* request_ids, int32_t n,
-                       int64_t* slots) {
+                       int64_t* slots, int32_t* copy_pairs, int32_t* num_copies) {
   if (!m) return PA_ERR_NULL;
   if (n < 0) return PA_ERR_SHAPE;
+  if (!num_copies) return PA_ERR_NULL;
+  *num_copies = 0;
   if (n == 0) return PA_OK;
-  if (!request_ids || !slots) return PA_ERR_NULL;
-  // Check everything first: known, distinct ids and enough free blocks for
-  // those at a block boundary -- then no append fails half-way.
+  if (!request_ids || !slots || !copy_pairs) return PA_ERR_NULL;
+  // Check everything first -- known, distinct ids and enough free blocks,
+  // the copies included, in batch order -- then no append fails half-way.
   int64_t need = 0;
   try {
     std::unordered_map<int64_t, int> seen;
+    std::unordered_map<int32_t, int> given_up;  // references dropped by earlier copies
     seen.reserve((size_t)n * 2);
     for (int32_t i = 0; i < n; ++i) {
       auto it = m->seqs.find(request_ids[i]);
       if (it == m->seqs.end() || !seen.emplace(request_ids[i], 1).second) return PA_ERR_RANGE;
-      need += it->second.len % m->block_size == 0;
+      const pa_block_manager::Seq& s = it->second;
+      const int32_t last = s.blocks.empty() ? -1 : s.blocks.back();
+      const int extra = last >= 0 && given_up.count(last) ? given_up[last] : 0;
+      const int k = blocks_needed(m, s, extra);
+      need += k;
+      if (k && s.len % m->block_size != 0) ++given_up[last];
     }
   } catch (...) {
     return PA_ERR_EXHAUSTED;
   }
   if (need > (int64_t)m->free_blocks.size()) return PA_ERR_EXHAUSTED;
+  int32_t nc = 0;
   for (int32_t i = 0; i < n; ++i) {
-    const int rc = pa_bm_append(m, request_ids[i], &slots[i]);
+    int32_t pair[2];
+    const int rc = append_one(m, m->seqs.find(request_ids[i])->second, &slots[i], pair);
     if (rc != PA_OK) return rc;  // not reached: checked above
+    if (pair[0] >= 0) {
+      copy_pairs[2 * nc] = pair[0];
+      copy_pairs[2 * nc + 1] = pair[1];
+      ++nc;
+    }
   }
+  *num_copies = nc;
   return PA_OK;
 }
 

@@ -61,6 +61,11 @@ hipError_t launch_reshape_and_cache(const void* key, const void* value, void* k_
                                     int num_kv_heads, int head_dim, int elem_bytes,
                                     int64_t num_blocks, hipStream_t stream);
 
+// Block copies inside both caches: pairs [num_pairs, 2] int32 (src, dst) on
+// the device; block_bytes = one block of one cache (all KV heads).
+hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int num_pairs,
+                              int64_t block_bytes, int64_t num_blocks, hipStream_t stream);
+
 // Vector-ALU decode: one workgroup per (query head, sequence, partition) item.
 hipError_t launch_decode_valu(const DecodeArgs& a, int dtype, int head_dim, hipStream_t stream);
 

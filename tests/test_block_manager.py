@@ -53,13 +53,31 @@ def test_reference_sharing_by_reference_count():
 def test_reference_append_takes_a_block_at_each_boundary():
     m = RefManager(6, BS)
     m.allocate(7, 15)
-    slots = [m.append(7) for _ in range(20)]       # tokens 15 .. 34
+    slots = [m.append(7)[0] for _ in range(20)]    # tokens 15 .. 34
     t = np.arange(15, 35)
     tab = m.table(7)
     assert len(tab) == 3 == -(-35 // BS)
     # slot of token t = table[t // 16] * 16 + t % 16 ("page_id * BLOCK_SIZE + page_offset")
     assert slots == [tab[i // BS] * BS + i % BS for i in t]
     assert m.num_free() == 3
+
+
+def test_reference_fork_copies_on_write():
+    """Two continuations of one 20-token prompt: both map its 2 blocks; the
+    first token either of them writes into the shared, partly filled block
+    moves that request onto a fresh block (the caller copies the shared one
+    there); the full first block stays shared."""
+    m = RefManager(6, BS)
+    m.allocate(1, 20)                              # blocks [0, 1], token 19 in block 1
+    m.fork(1, 2)
+    assert m.refcount[0] == m.refcount[1] == 2
+    slot, copy = m.append(2)                       # token 20 would land in block 1
+    assert copy == (1, 2) and m.table(2) == [0, 2] and slot == 2 * BS + 20 % BS
+    assert m.refcount[1] == 1 and m.refcount[0] == 2
+    slot, copy = m.append(1)                       # request 1 now owns block 1 alone
+    assert copy is None and slot == 1 * BS + 20 % BS and m.table(1) == [0, 1]
+    m.free(1)
+    assert m.refcount[0] == 1 and 1 in m.free_blocks and 0 not in m.free_blocks
 
 
 def _invariants(m: RefManager):
@@ -90,6 +108,10 @@ def random_ops(seed, n_ops=400, num_blocks=40):
             ops.append(("share", int(rng.choice(live)), next_id, int(rng.integers(0, 4))))
             live.append(next_id)
             next_id += 1
+        elif r < 0.47:
+            ops.append(("fork", int(rng.choice(live)), next_id))
+            live.append(next_id)
+            next_id += 1
         elif r < 0.85:
             ops.append(("append", int(rng.choice(live))))
         else:
@@ -107,6 +129,9 @@ def apply(m, op, exhausted, invalid):
             return ("ok",)
         if kind == "share":
             m.share(op[1], op[2], op[3])
+            return ("ok",)
+        if kind == "fork":
+            m.fork(op[1], op[2])
             return ("ok",)
         if kind == "append":
             return ("slot", m.append(op[1]))
@@ -172,14 +197,20 @@ def test_library_manager_argument_checks(hiplib):
 
 def test_library_append_batch_matches_sequential_appends(hiplib):
     from paged_kv_cache_269_amd import BlockManager, KVCacheExhausted, PagedAttnError
-    ref, lib = RefManager(12, BS), BlockManager(12, BS)
+    ref, lib = RefManager(20, BS), BlockManager(20, BS)
     for rid, n in ((0, 16), (1, 5), (2, 31)):
         ref.allocate(rid, n)
         lib.allocate(rid, n)
+    ref.fork(2, 3)
+    lib.fork(2, 3)
     for _ in range(20):
-        want = [ref.append(r) for r in (2, 0, 1)]
-        assert lib.append_batch([2, 0, 1]).tolist() == want
+        want = [ref.append(r) for r in (2, 0, 3, 1)]
+        slots, copies = lib.append_batch([2, 0, 3, 1])
+        assert slots.tolist() == [w[0] for w in want]
+        assert [tuple(c) for c in copies.tolist()] == [w[1] for w in want if w[1] is not None]
     assert lib.free_blocks().tolist() == list(ref.free_blocks)
+    lib.free(3)
+    ref.free(3)
     with pytest.raises(PagedAttnError):
         lib.append_batch([0, 0])             # repeated id: nothing changes
     with pytest.raises(PagedAttnError):
@@ -194,3 +225,12 @@ def test_library_append_batch_matches_sequential_appends(hiplib):
             assert [lib.seq_len(r) for r in (0, 1, 2)] == lens
             break
     lib.close()
+
+
+def test_copy_validator(hiplib):
+    ok = np.array([[0, 5], [1, 6], [0, 7]])
+    assert hiplib.validate_copy_host(ok, 8) == 0
+    assert hiplib.validate_copy_host([[0, 5], [1, 5]], 8) == 5      # repeated destination
+    assert hiplib.validate_copy_host([[0, 5], [5, 6]], 8) == 5      # destination used as source
+    assert hiplib.validate_copy_host([[0, 8]], 8) == 5              # outside the pool
+    assert hiplib.validate_copy_host(np.zeros((0, 2)), 8) == 0

@@ -67,7 +67,7 @@ def test_multistep_decode_with_block_manager(cuda, dtype, Hq, Hkv):
         oracle.reshape_and_cache(k, v, kh, vh, sl, dtype)
 
     def prompt(rid, n):
-        write([bm.append(rid) for _ in range(n)])
+        write([bm.append(rid)[0] for _ in range(n)])
 
     bm.allocate(0, 0)
     prompt(0, 80)                      # 5 blocks
@@ -90,7 +90,7 @@ def test_multistep_decode_with_block_manager(cuda, dtype, Hq, Hkv):
             bm.allocate(5, 0)          # takes blocks request 3 left
             prompt(5, 50)
             live.append(5)
-        write([bm.append(r) for r in live])
+        write([bm.append(r)[0] for r in live])
         bt, cl = bm.block_tables(live, M, pad=0)
         q = rand_rows(rng, (len(live), Hq, D), dtype)
         qd, btd, cld = to_dev(q, dtype, cuda), torch.from_numpy(bt).to(cuda), torch.from_numpy(cl).to(cuda)
