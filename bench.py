@@ -51,6 +51,9 @@ def parse_args(argv=None):
     ap.add_argument("--loop-steps", type=int, default=0,
                     help="also time this many steps of a multi-step decode loop driven by the "
                          "host block manager (one new token per sequence per step)")
+    ap.add_argument("--block-ops", action="store_true",
+                    help="also time pa_copy_blocks (device) and pa_swap_blocks (device <-> "
+                         "pinned host) on blocks of this workload's pool")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB before warmup, as the "
                          "known-size reference for HBM byte counters")
@@ -236,6 +239,65 @@ def decode_loop(args, w, dev):
                     "graph (packed H2D copy, reshape_and_cache, decode)"}
 
 
+def block_ops(w, dev):
+    """Copy-on-write copies and swaps on this workload's block shape: 2048
+    random (src, dst) pairs copied inside the pool (both caches), and 1024
+    blocks of the K cache swapped out to pinned host memory and back."""
+    import numpy as np
+    import torch
+    import paged_kv_cache_269_amd as pa
+    from paged_kv_cache_269_amd import workloads as W
+
+    Hkv, D = w.num_kv_heads, w.head_dim
+    tdt = W.torch_dtype(w.dtype)
+    N = 8192
+    kc = torch.randn((N, Hkv, 16, D), device=dev).to(tdt)
+    vc = torch.randn((N, Hkv, 16, D), device=dev).to(tdt)
+    block_bytes = kc[0].numel() * kc.element_size()
+    rng = np.random.default_rng(0)
+    perm = rng.permutation(N)
+    pairs = torch.from_numpy(np.stack([perm[:2048], perm[2048:4096]], 1).astype(np.int32)).to(dev)
+    for _ in range(3):
+        pa.copy_blocks(kc, vc, pairs)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 20
+    e0.record()
+    for _ in range(reps):
+        pa.copy_blocks(kc, vc, pairs)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_us = e0.elapsed_time(e1) * 1e3 / reps
+    copy_bytes = 2 * 2 * 2048 * block_bytes          # read + write, K and V
+    host = torch.empty((1024, Hkv, 16, D), dtype=tdt).pin_memory()
+    out_pairs = np.stack([perm[4096:5120], rng.permutation(1024)], 1)   # scattered, no runs
+    in_pairs = out_pairs[:, ::-1].copy()
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(5):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / 5
+
+    out_us = timed(lambda: pa.swap_blocks(kc, host, out_pairs))
+    in_us = timed(lambda: pa.swap_blocks(host, kc, in_pairs))
+    sw_bytes = 1024 * block_bytes
+    return {"block_bytes_per_cache": block_bytes,
+            "copy_pairs": 2048, "copy_us": round(copy_us, 2),
+            "copy_GBps": round(copy_bytes / copy_us / 1e3, 1),
+            "copy_frac_of_hbm_peak": round(copy_bytes / copy_us / 1e3 / HBM_PEAK_GBPS, 4),
+            "swap_blocks": 1024, "swap_out_us": round(out_us, 1), "swap_in_us": round(in_us, 1),
+            "swap_out_GBps": round(sw_bytes / out_us / 1e3, 1),
+            "swap_in_GBps": round(sw_bytes / in_us / 1e3, 1),
+            "note": "copy: read + write of K and V blocks; swap: one cache, scattered blocks, "
+                    "one asynchronous copy each"}
+
+
 def main(argv=None) -> int:
     args = parse_args(argv)
     if args.gpus != 1:
@@ -364,6 +426,8 @@ def main(argv=None) -> int:
                      "launch_us_p90": round(float(np.percentile(dec_ms, 90)) * 1e3, 2),
                      "algorithmic_bytes_per_launch": ab["total"]},
     }
+    if args.block_ops:
+        result["block_ops"] = block_ops(w, dev)
     if args.loop_steps > 0:
         del pools, d, ws
         torch.cuda.empty_cache()

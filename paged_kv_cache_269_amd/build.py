@@ -13,7 +13,7 @@ LIB_PATH = os.path.join(HERE, "libpagedattn.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "block_manager.cpp", "reshape_and_cache.hip", "copy_blocks.hip",
+SOURCES = ["api.cpp", "api_blocks.cpp", "block_manager.cpp", "reshape_and_cache.hip", "copy_blocks.hip",
            "decode_valu.hip", "decode_mfma.hip", "prefix.hip", "reduce.hip"]
 
 # Packed fp32 ALU ops are kept out of the generated code.  Matrix-core

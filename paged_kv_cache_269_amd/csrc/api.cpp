@@ -276,65 +276,6 @@ int pa_paged_attention_reduce(void* out, const float* max_logits, const float* e
   return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
-int pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_pairs, int32_t num_pairs,
-                   int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
-                   int32_t dtype, void* stream) {
-  const int eb = elem_bytes(dtype);
-  if (!eb || block_size != kBlock || !head_dim_ok(head_dim)) return PA_ERR_UNSUPPORTED;
-  if (num_pairs < 0 || num_pairs > kMaxGridYZ || num_kv_heads <= 0 || num_blocks <= 0)
-    return PA_ERR_SHAPE;
-  if (num_pairs == 0) return PA_OK;
-  if (!k_cache || !v_cache || !block_pairs) return PA_ERR_NULL;
-  const int64_t block_bytes = (int64_t)num_kv_heads * kBlock * head_dim * eb;
-  hipError_t e = pa::launch_copy_blocks(k_cache, v_cache, block_pairs, num_pairs, block_bytes,
-                                        num_blocks, (hipStream_t)stream);
-  return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
-}
-
-int pa_swap_blocks(const void* src_cache, void* dst_cache, const int64_t* block_pairs,
-                   int32_t num_pairs, int64_t block_bytes, void* stream) {
-  if (num_pairs < 0 || block_bytes <= 0) return PA_ERR_SHAPE;
-  if (num_pairs == 0) return PA_OK;
-  if (!src_cache || !dst_cache || !block_pairs) return PA_ERR_NULL;
-  for (int32_t i = 0; i < num_pairs; ++i)
-    if (block_pairs[2 * i] < 0 || block_pairs[2 * i + 1] < 0) return PA_ERR_RANGE;
-  const char* src = static_cast<const char*>(src_cache);
-  char* dst = static_cast<char*>(dst_cache);
-  // Runs of pairs whose source and destination blocks both advance by one
-  // move as one copy.
-  for (int32_t i = 0; i < num_pairs;) {
-    int32_t j = i + 1;
-    while (j < num_pairs && block_pairs[2 * j] == block_pairs[2 * (j - 1)] + 1 &&
-           block_pairs[2 * j + 1] == block_pairs[2 * (j - 1) + 1] + 1)
-      ++j;
-    const hipError_t e = hipMemcpyAsync(dst + block_pairs[2 * i + 1] * block_bytes,
-                                        src + block_pairs[2 * i] * block_bytes,
-                                        (size_t)(j - i) * block_bytes, hipMemcpyDefault,
-                                        (hipStream_t)stream);
-    if (e != hipSuccess) return PA_ERR_LAUNCH;
-    i = j;
-  }
-  return PA_OK;
-}
-
-int pa_validate_copy_host(const int32_t* block_pairs, int32_t num_pairs, int64_t num_blocks) {
-  if (num_pairs < 0 || num_blocks < 0) return PA_ERR_SHAPE;
-  if (num_pairs == 0) return PA_OK;
-  if (!block_pairs) return PA_ERR_NULL;
-  std::vector<int32_t> dst(num_pairs), src(num_pairs);
-  for (int32_t i = 0; i < num_pairs; ++i) {
-    src[i] = block_pairs[2 * i];
-    dst[i] = block_pairs[2 * i + 1];
-    if (src[i] < 0 || src[i] >= num_blocks || dst[i] < 0 || dst[i] >= num_blocks)
-      return PA_ERR_RANGE;
-  }
-  std::sort(dst.begin(), dst.end());
-  if (std::adjacent_find(dst.begin(), dst.end()) != dst.end()) return PA_ERR_RANGE;
-  for (int32_t s : src)
-    if (std::binary_search(dst.begin(), dst.end(), s)) return PA_ERR_RANGE;
-  return PA_OK;
-}
-
 int pa_validate_tables_host(const int32_t* block_tables, const int32_t* context_lens,
                             int32_t num_seqs, int32_t max_blocks_per_seq, int64_t num_blocks,
                             int32_t block_size) {
