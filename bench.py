@@ -39,6 +39,9 @@ def parse_args(argv=None):
                     help="workload: tiny, llama7b, gqa, shared_prefix, long_context")
     ap.add_argument("--partition-size", type=int, default=None,
                     help="override the workload's partition size (0 = single pass)")
+    ap.add_argument("--block-size", type=int, default=None,
+                    help="lay the pool out in blocks of this many tokens (8, 16, 32; default: "
+                         "the workload's 16)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
@@ -317,7 +320,7 @@ def main(argv=None) -> int:
     dev = torch.device("cuda:0")
     pa.load_library()
 
-    w = W.generate(args.config, poison=False)
+    w = W.generate(args.config, poison=False, block_size=args.block_size)
     part = w.partition_size if args.partition_size is None else args.partition_size
     d = W.to_device(w, dev)
     pools = [(d["k_cache"], d["v_cache"])]
@@ -400,7 +403,8 @@ def main(argv=None) -> int:
         "dtype": w.dtype,
         "data": "synthetic (seeded N(0,1) q/K/V, randomly permuted 16-token blocks)",
         "config": {"workload": w.name, "num_seqs": w.num_seqs, "num_q_heads": w.num_q_heads,
-                   "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "block_size": 16,
+                   "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
+                   "block_size": w.block_size,
                    "kv_dtype": w.dtype, "accumulate": "f32", "partition_size": part,
                    "context_len_mean": float(w.context_lens.mean()),
                    "context_len_max": int(w.max_context_len), "num_blocks": w.num_blocks,

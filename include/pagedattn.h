@@ -29,8 +29,10 @@
  *       block_tables       [num_seqs, max_blocks_per_seq] int32
  *       context_lens       [num_seqs] int32
  *       slot_mapping       [num_tokens] int64
- *     Logical token t of sequence s lives in block block_tables[s][t / 16]
- *     at offset t % 16.  context_lens[s] counts every cached token, the one
+ *     Logical token t of sequence s lives in block block_tables[s][t / bs]
+ *     at offset t % bs (bs = block_size: 16 by default, 8 or 32 also taken;
+ *     [DM] block-size notes: 16 default, 8 and 32 as tuning choices).
+ *     context_lens[s] counts every cached token, the one
  *     being decoded included.  Query head h reads KV head
  *     h / (num_q_heads / num_kv_heads).
  *   - Pointers are device pointers on the current HIP device, owned by the
@@ -64,7 +66,7 @@ enum pa_status {
   PA_ERR_SHAPE = 2,       /* a size is out of range (num_seqs, num_q_heads and the
                              partition count are limited to 65535), or
                              num_q_heads % num_kv_heads != 0 */
-  PA_ERR_UNSUPPORTED = 3, /* head_dim not 64/128, block_size not 16, unknown dtype,
+  PA_ERR_UNSUPPORTED = 3, /* head_dim not 64/128, block_size not 8/16/32, unknown dtype,
                              partition_size not a positive multiple of 16 (or 0) */
   PA_ERR_WORKSPACE = 4,   /* workspace missing or smaller than pa_decode_workspace_bytes
                              (pa_cascade_workspace_bytes for the cascade entry point) */
@@ -77,11 +79,11 @@ enum pa_status {
  * KV write ([CX] §1.1: the new tokens' K and V are stored in the cache;
  * [CX] §2.2: token address = block * 16 + offset).  For each token i with
  * 0 <= slot = slot_mapping[i] < 16 * num_blocks:
- *     k_cache[slot / 16, h, slot % 16, :] = key[i, h, :]   for every h
- *     v_cache[slot / 16, h, slot % 16, :] = value[i, h, :]
+ *     k_cache[slot / bs, h, slot % bs, :] = key[i, h, :]   for every h
+ *     v_cache[slot / bs, h, slot % bs, :] = value[i, h, :]
  * A bit copy.  Negative slots mean "no write" (padding).  Two tokens with
  * the same slot leave either one's row in it (a caller error).
- * block_size must be 16; head_dim 64 or 128.  num_tokens = 0 is a no-op.
+ * block_size (bs) 8, 16 or 32; head_dim 64 or 128.  num_tokens = 0 is a no-op.
  */
 int pa_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
                          const int64_t* slot_mapping, int32_t num_tokens,
@@ -91,9 +93,9 @@ int pa_reshape_and_cache(const void* key, const void* value, void* k_cache, void
 /*
  * Decode attention over the paged cache ([CX] §1.1, §2.1-§2.2; [MJ] §2.2):
  * for every sequence s and query head h, with L = context_lens[s],
- * g = h / (num_q_heads / num_kv_heads), b_t = block_tables[s][t / 16]:
- *     z_t = scale * sum_d q[s,h,d] * k_cache[b_t, g, t % 16, d]
- *     out[s,h,:] = sum_{t<L} exp(z_t - max z) v_cache[b_t, g, t % 16, :]
+ * g = h / (num_q_heads / num_kv_heads), b_t = block_tables[s][t / bs]:
+ *     z_t = scale * sum_d q[s,h,d] * k_cache[b_t, g, t % bs, d]
+ *     out[s,h,:] = sum_{t<L} exp(z_t - max z) v_cache[b_t, g, t % bs, :]
  *                  / sum_{t<L} exp(z_t - max z)
  * rounded to nearest-even into out's type.  L = 0 gives a zero row.
  *
@@ -109,7 +111,10 @@ int pa_reshape_and_cache(const void* key, const void* value, void* k_cache, void
  * that share a workspace must not run concurrently.
  * max_context_len is a host-side bound on context_lens (sizes the grid);
  * longer contexts are clamped to it.  Tail slots of a sequence's last block
- * and blocks past ceil(L / 16) are never used, whatever they hold.
+ * and blocks past ceil(L / bs) are never used, whatever they hold.
+ * block_size 8 or 32 runs the workgroup-per-item kernels for every
+ * partition count (the one-wave and streaming forms are 16-token only);
+ * partition_size stays a multiple of 16 tokens.
  */
 int pa_paged_attention_decode(void* out, const void* q, const void* k_cache,
                               const void* v_cache, const int32_t* block_tables,
@@ -163,7 +168,8 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
  * matrix-core tile; each sequence's remaining blocks are then processed as in
  * pa_paged_attention_decode and the two parts merged by the log-sum-exp rule
  * of pa_paged_attention_reduce.  Runs that share fewer blocks are decoded as
- * usual; float32, G > 8 or num_seqs < 2 skip the shared part altogether.
+ * usual; float32, G > 8, num_seqs < 2 or a block size other than 16 skip the
+ * shared part altogether.
  *
  * `workspace` (device memory, caller-owned) must hold at least
  * pa_cascade_workspace_bytes(num_seqs, num_q_heads, head_dim) bytes: it

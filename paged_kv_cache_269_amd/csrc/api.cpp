@@ -17,7 +17,10 @@ namespace {
 #define PA_MFMA_MIN_GROUP 2  // smallest head group sent to the matrix-core kernel
 #endif
 
-constexpr int kBlock = 16;
+constexpr int kBlock = 16;  // tokens per kernel tile; partitions are multiples of it
+
+// Pool block sizes the kernels take (tokens per block).
+bool block_size_ok(int32_t bs) { return bs == 8 || bs == 16 || bs == 32; }
 constexpr int kMaxGridYZ = 65535;
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -88,7 +91,7 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
                 int32_t max_blocks_per_seq, int64_t num_blocks, float scale, int32_t dtype,
                 int32_t partition_size, int32_t max_context_len, void* workspace,
                 size_t workspace_bytes, void* stream, bool cascade) {
-  if (!elem_bytes(dtype) || block_size != kBlock || !head_dim_ok(head_dim))
+  if (!elem_bytes(dtype) || !block_size_ok(block_size) || !head_dim_ok(head_dim))
     return PA_ERR_UNSUPPORTED;
   if (partition_size < 0 || partition_size % kBlock) return PA_ERR_UNSUPPORTED;
   if (num_seqs < 0 || num_seqs > kMaxGridYZ || num_q_heads <= 0 || num_q_heads > kMaxGridYZ ||
@@ -99,7 +102,8 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return PA_ERR_NULL;
 
   // Longest context any kernel will look at.
-  const int64_t max_len = std::min<int64_t>(max_context_len, (int64_t)max_blocks_per_seq * kBlock);
+  const int64_t max_len =
+      std::min<int64_t>(max_context_len, (int64_t)max_blocks_per_seq * block_size);
   const int64_t table_blocks = ceil_div(std::max<int64_t>(max_len, 1), kBlock);
   int64_t part_blocks, parts;
   if (partition_size == 0) {
@@ -136,13 +140,15 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   a.part_blocks = (int)part_blocks;
   a.max_partitions = (int)parts;
   a.scale_log2 = scale * 1.4426950408889634f;
+  a.block_size = block_size;
 
   const hipStream_t st = (hipStream_t)stream;
   const int group = num_q_heads / num_kv_heads;
   // Grouped heads share every K/V tile: a matrix-core product pays off from
   // two heads up.  Single heads and fp32 stay on the vector ALU.
   const bool use_mfma = dtype != PA_F32 && group >= PA_MFMA_MIN_GROUP;
-  if (cascade && dtype != PA_F32 && group <= kCascadeMaxGroup && num_seqs >= 2) {
+  if (cascade && dtype != PA_F32 && group <= kCascadeMaxGroup && num_seqs >= 2 &&
+      block_size == kBlock) {
     // Shared-prefix pass first; the decode kernel then covers each
     // sequence's remaining blocks and merges the two parts.
     char* c = static_cast<char*>(workspace);
@@ -187,7 +193,8 @@ const char* pa_status_string(int status) {
     case PA_OK: return "ok";
     case PA_ERR_NULL: return "a required pointer is NULL";
     case PA_ERR_SHAPE: return "a size is out of range or num_q_heads is not a multiple of num_kv_heads";
-    case PA_ERR_UNSUPPORTED: return "unsupported head_dim, block_size, dtype or partition_size";
+    case PA_ERR_UNSUPPORTED:
+      return "unsupported head_dim (64, 128), block_size (8, 16, 32), dtype or partition_size";
     case PA_ERR_WORKSPACE: return "workspace missing or too small";
     case PA_ERR_RANGE: return "table entry, context length or slot out of range";
     case PA_ERR_LAUNCH: return "the HIP runtime refused a kernel launch";
@@ -210,13 +217,13 @@ int pa_reshape_and_cache(const void* key, const void* value, void* k_cache, void
                          int32_t head_dim, int32_t block_size, int64_t num_blocks, int32_t dtype,
                          void* stream) {
   const int eb = elem_bytes(dtype);
-  if (!eb || block_size != kBlock || !head_dim_ok(head_dim)) return PA_ERR_UNSUPPORTED;
+  if (!eb || !block_size_ok(block_size) || !head_dim_ok(head_dim)) return PA_ERR_UNSUPPORTED;
   if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks <= 0) return PA_ERR_SHAPE;
   if (num_tokens == 0) return PA_OK;
   if (!key || !value || !k_cache || !v_cache || !slot_mapping) return PA_ERR_NULL;
   hipError_t e = pa::launch_reshape_and_cache(key, value, k_cache, v_cache, slot_mapping,
-                                              num_tokens, num_kv_heads, head_dim, eb, num_blocks,
-                                              (hipStream_t)stream);
+                                              num_tokens, num_kv_heads, head_dim, eb, block_size,
+                                              num_blocks, (hipStream_t)stream);
   return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 

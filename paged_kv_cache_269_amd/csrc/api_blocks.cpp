@@ -13,7 +13,6 @@
 
 namespace {
 
-constexpr int kBlock = 16;
 constexpr int kMaxGridYZ = 65535;
 
 int elem_bytes(int32_t dtype) {
@@ -35,12 +34,13 @@ int pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_pairs, int
                    int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
                    int32_t dtype, void* stream) {
   const int eb = elem_bytes(dtype);
-  if (!eb || block_size != kBlock || !head_dim_ok(head_dim)) return PA_ERR_UNSUPPORTED;
+  if (!eb || !(block_size == 8 || block_size == 16 || block_size == 32) || !head_dim_ok(head_dim))
+    return PA_ERR_UNSUPPORTED;
   if (num_pairs < 0 || num_pairs > kMaxGridYZ || num_kv_heads <= 0 || num_blocks <= 0)
     return PA_ERR_SHAPE;
   if (num_pairs == 0) return PA_OK;
   if (!k_cache || !v_cache || !block_pairs) return PA_ERR_NULL;
-  const int64_t block_bytes = (int64_t)num_kv_heads * kBlock * head_dim * eb;
+  const int64_t block_bytes = (int64_t)num_kv_heads * block_size * head_dim * eb;
   hipError_t e = pa::launch_copy_blocks(k_cache, v_cache, block_pairs, num_pairs, block_bytes,
                                         num_blocks, (hipStream_t)stream);
   return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;

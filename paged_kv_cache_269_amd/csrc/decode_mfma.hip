@@ -97,7 +97,7 @@ __device__ __forceinline__ void mark_empty(const DecodeArgs& a, const HeadTile& 
 // writes its result from registers (no merge, no barrier); otherwise the NW
 // waves share the partition's blocks and merge through LDS.  `kst` is the
 // calling wave's K staging tile.
-template <int DT, int D, int NW, int DEPTH, bool WAVE_ITEM>
+template <int DT, int D, int NW, int DEPTH, bool WAVE_ITEM, int BS = kBlockSize>
 __device__ __forceinline__ void mfma_item(const DecodeArgs& a, const int unit, const int s,
                                           const int part, const int L, MfmaLds<D, NW>* sm,
                                           u32x4* kst) {
@@ -131,15 +131,18 @@ __device__ __forceinline__ void mfma_item(const DecodeArgs& a, const int unit, c
   MfmaState<D> st;
   st.reset();
 
-  // Pool id of the wave's kk-th block (index clamped into the table row).
-  auto id_at = [&](int kk) -> int { return bt[j0 + min(kk, nk - 1) * STRIDE]; };
+  // Pool ids of the wave's kk-th 16-token tile (index clamped into the row).
+  auto id_at = [&](int kk) {
+    return tile_ids<BS>(bt, j0 + min(kk, nk - 1) * STRIDE, a.max_blocks_per_seq);
+  };
   // Descriptors of the wave's kk-th tile and the number of its tokens in the
-  // context; empty past the wave's last block or for an id outside the pool.
-  auto tile = [&](int kk, int bid, int& limit, Rsrc& rk, Rsrc& rv) {
+  // context; empty past the wave's last tile, and tokens in a block outside
+  // the pool do not count.
+  auto tile = [&](int kk, const TileIds<BS>& ids, int& limit) {
     const int j = j0 + min(kk, nk - 1) * STRIDE;
-    const bool ok = kk < nk && (uint32_t)bid < (uint32_t)a.num_blocks_i32;
-    limit = ok ? min(kBlockSize, L - j * kBlockSize) : 0;
-    tile_rsrc<DT, D>(a, bid, t.kvh, ok, rk, rv);
+    const bool ok = kk < nk;
+    limit = ok ? tile_limit<BS>(a, ids, L - j * kBlockSize) : 0;
+    return tile_desc<BS, S::TILE_BYTES>(a, ids, j, t.kvh, ok);
   };
 
   // Software pipeline over the wave's blocks: DEPTH register sets; while
@@ -155,21 +158,17 @@ __device__ __forceinline__ void mfma_item(const DecodeArgs& a, const int unit, c
     constexpr bool SH = decltype(shared)::value;
     static_for<0, DEPTH - 1>([&](auto dc) {
       constexpr int d = decltype(dc)::value;
-      Rsrc rk, rv;
-      tile(d, id_at(d), lim[d], rk, rv);
-      load_tile<DT, D, SH>(rk, rv, ln, kr[d], vr[d]);
+      load_tile<DT, D, SH>(tile(d, id_at(d), lim[d]), ln, kr[d], vr[d]);
     });
-    int next_id = id_at(DEPTH - 1);
+    TileIds<BS> next_id = id_at(DEPTH - 1);
     for (int k = 0; k < nk; k += DEPTH) {
       static_for<0, DEPTH>([&](auto dc) {
         constexpr int d = decltype(dc)::value;
         constexpr int dn = (d + DEPTH - 1) % DEPTH;
-        const int kn = k + d + DEPTH - 1;  // block whose loads are issued now
-        const int id = next_id;
+        const int kn = k + d + DEPTH - 1;  // tile whose loads are issued now
+        const TileIds<BS> id = next_id;
         next_id = id_at(kn + 1);
-        Rsrc rk, rv;
-        tile(kn, id, lim[dn], rk, rv);
-        load_tile<DT, D, SH>(rk, rv, ln, kr[dn], vr[dn]);
+        load_tile<DT, D, SH>(tile(kn, id, lim[dn]), ln, kr[dn], vr[dn]);
         consume_any<DT, D>(st, qb, kr[d], vr[d], lim[d], a.scale_log2, ln, kst);
       });
     }
@@ -181,7 +180,8 @@ __device__ __forceinline__ void mfma_item(const DecodeArgs& a, const int unit, c
     // items stream their tiles non-temporally.
     const int32_t* nb = a.num_seqs > 1 ? a.block_tables +
                             (int64_t)(s > 0 ? s - 1 : s + 1) * a.max_blocks_per_seq : nullptr;
-    if (nb != nullptr && nb[j0] == bt[j0])
+    if (nb != nullptr && tile_ids<BS>(nb, j0, a.max_blocks_per_seq).id[0] ==
+                             tile_ids<BS>(bt, j0, a.max_blocks_per_seq).id[0])
       pipeline(std::true_type{});
     else
       pipeline(std::false_type{});
@@ -250,7 +250,7 @@ __device__ __forceinline__ void mfma_item(const DecodeArgs& a, const int unit, c
 // workgroups are dealt to the 8 XCDs round-robin, so the equal-sized items of
 // one (sequence, partition) spread evenly over the XCDs, and one head unit of
 // every sequence stays on one XCD (shared prefix pages then hit its L2).
-template <int DT, int D, int NW, int DEPTH>
+template <int DT, int D, int NW, int DEPTH, int BS>
 __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
   __shared__ MfmaLds<D, NW> sm;
   __shared__ u32x4 kst[NW][kKStageSlots<D>];
@@ -258,7 +258,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
   const int L = clamp_len(a, s);
   if (part >= parts_of(L, a.part_blocks)) return;  // past this sequence's end
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  mfma_item<DT, D, NW, DEPTH, false>(a, unit, s, part, L, &sm, kst[w]);
+  mfma_item<DT, D, NW, DEPTH, false, BS>(a, unit, s, part, L, &sm, kst[w]);
 }
 
 // One wave per item: wave w of workgroup z takes partition z * NW + w, for
@@ -419,10 +419,10 @@ __global__ __launch_bounds__(NW * 64, PA_STREAM_MIN_WAVES) void decode_mfma_stre
   auto issue = [&](int slot, int bid) {
     const bool live = lc.left > 0;
     const bool ok = live && lc.j < lc.nblocks && (uint32_t)bid < (uint32_t)a.num_blocks_i32;
-    Rsrc rk, rv;
-    tile_rsrc<DT, D>(a, bid, lc.kvh, ok, rk, rv);
     lim[slot] = ok ? min(kBlockSize, lc.len - lc.j * kBlockSize) : 0;
-    load_tile<DT, D, false>(rk, rv, ln, kr[slot], vr[slot]);
+    load_tile<DT, D, false>(tile_desc<kBlockSize, S::TILE_BYTES>(a, TileIds<kBlockSize>{{bid}},
+                                                                 lc.j, lc.kvh, ok),
+                            ln, kr[slot], vr[slot]);
     if (live) lc.advance(a, tables, lens, units, hchunks);
   };
   auto id_of = [&](const StreamCursor& c) -> int {
@@ -488,11 +488,12 @@ __global__ __launch_bounds__(NW * 64, PA_STREAM_MIN_WAVES) void decode_mfma_stre
 // shorter ones 4 (more workgroups resident per CU).
 constexpr int kLongItemBlocks = 128;
 
-template <int DT, int D, int NW, int DEPTH>
+template <int DT, int D, int NW, int DEPTH, int BS = kBlockSize>
 hipError_t launch_shape(const DecodeArgs& a, hipStream_t stream) {
   const int group = a.num_q_heads / a.num_kv_heads;
   const dim3 grid(a.num_kv_heads * ((group + 15) / 16), a.num_seqs, a.max_partitions);
-  hipLaunchKernelGGL((decode_mfma_kernel<DT, D, NW, DEPTH>), grid, dim3(NW * 64), 0, stream, a);
+  hipLaunchKernelGGL((decode_mfma_kernel<DT, D, NW, DEPTH, BS>), grid, dim3(NW * 64), 0, stream,
+                     a);
   return hipGetLastError();
 }
 
@@ -547,6 +548,13 @@ hipError_t launch_stream_shape(const DecodeArgs& a, int64_t items, hipStream_t s
 
 template <int DT, int D>
 hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
+  // 8- and 32-token blocks: workgroup-per-item kernels for every launch.
+  if (a.block_size == 8)
+    return a.part_blocks >= kLongItemBlocks ? launch_shape<DT, D, 8, 2, 8>(a, stream)
+                                            : launch_shape<DT, D, 4, 2, 8>(a, stream);
+  if (a.block_size == 32)
+    return a.part_blocks >= kLongItemBlocks ? launch_shape<DT, D, 8, 2, 32>(a, stream)
+                                            : launch_shape<DT, D, 4, 2, 32>(a, stream);
   const int group = a.num_q_heads / a.num_kv_heads;
   const int64_t items = (int64_t)a.num_kv_heads * ((group + 15) / 16) * a.num_seqs *
                         a.max_partitions;

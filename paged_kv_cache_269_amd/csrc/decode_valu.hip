@@ -58,7 +58,7 @@ struct ValuLds {
 // WAVE_ITEM: the calling wave alone processes the whole partition and merges
 // its rows in registers (no LDS, no barrier); otherwise the NW waves of the
 // workgroup share the partition's blocks and merge through LDS.
-template <int DT, int D, int NW, int DEPTH, bool WAVE_ITEM>
+template <int DT, int D, int NW, int DEPTH, bool WAVE_ITEM, int BS = kBlockSize>
 __device__ __forceinline__ void valu_item(const DecodeArgs& a, const int h, const int s,
                                           const int part, const int L, ValuLds<DT, D, NW>* sm) {
   using S = ValuShape<DT, D>;
@@ -79,8 +79,6 @@ __device__ __forceinline__ void valu_item(const DecodeArgs& a, const int h, cons
   }
 
   const u32x4 qv = reinterpret_cast<const u32x4*>(a.q)[orow * (D / VEC) + c];
-  const char* kbase = static_cast<const char*>(a.k_cache);
-  const char* vbase = static_cast<const char*>(a.v_cache);
   const int32_t* __restrict__ bt = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
   // Shared-prefix launches (one pass): the leading `pre` blocks were done by
   // the prefix kernel; their state joins the merge below.
@@ -96,25 +94,34 @@ __device__ __forceinline__ void valu_item(const DecodeArgs& a, const int h, cons
 #pragma unroll
   for (int k = 0; k < VEC; ++k) acc[k] = 0.f;
 
-  // Pool id of the wave's kk-th block (index clamped into the table row).
-  auto id_at = [&](int kk) -> int { return bt[j0 + min(kk, nk - 1) * STRIDE]; };
-  // Descriptors of the wave's kk-th tile and the number of its tokens in the
-  // context; past the wave's last block, or for an id outside the pool, the
-  // descriptors are empty and no token counts.
-  auto tile = [&](int kk, int bid, int& limit, Rsrc& rk, Rsrc& rv) {
-    const int j = j0 + min(kk, nk - 1) * STRIDE;
-    const bool ok = kk < nk && (uint32_t)bid < (uint32_t)a.num_blocks_i32;
-    limit = ok ? min(kBlockSize, L - j * kBlockSize) : 0;
-    const int64_t off = ((int64_t)(ok ? bid : 0) * a.num_kv_heads + kvh) * S::TILE_BYTES;
-    rk = make_rsrc(kbase + off, ok ? S::TILE_BYTES : 0);
-    rv = make_rsrc(vbase + off, ok ? S::TILE_BYTES : 0);
+  using Desc = TileDesc<BS, S::TILE_BYTES>;
+  // Pool ids of the wave's kk-th 16-token tile (index clamped into the row).
+  auto id_at = [&](int kk) {
+    return tile_ids<BS>(bt, j0 + min(kk, nk - 1) * STRIDE, a.max_blocks_per_seq);
   };
-  auto load = [&](auto shared, Rsrc rk, Rsrc rv, u32x4 (&kr)[NLD], u32x4 (&vr)[NLD]) {
+  // Descriptors of the wave's kk-th tile and the number of its tokens in the
+  // context; past the wave's last tile the descriptors are empty and no
+  // token counts, nor do tokens in a block whose id lies outside the pool.
+  auto tile = [&](int kk, const TileIds<BS>& ids, int& limit) {
+    const int j = j0 + min(kk, nk - 1) * STRIDE;
+    const bool ok = kk < nk;
+    limit = ok ? tile_limit<BS>(a, ids, L - j * kBlockSize) : 0;
+    return tile_desc<BS, S::TILE_BYTES>(a, ids, j, kvh, ok);
+  };
+  // Load i covers the tile's i-th KiB (TPL whole rows); which block part it
+  // reads is known per load at compile time.
+  auto load = [&](auto shared, const Desc& t, u32x4 (&kr)[NLD], u32x4 (&vr)[NLD]) {
     constexpr bool SH = decltype(shared)::value;
-#pragma unroll
-    for (int i = 0; i < NLD; ++i) kr[i] = buf_load16<SH>(rk, (i * 64 + lane) * 16);
-#pragma unroll
-    for (int i = 0; i < NLD; ++i) vr[i] = buf_load16<SH>(rv, (i * 64 + lane) * 16);
+    static_for<0, NLD>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      constexpr int h = Desc::part(i * 1024);
+      kr[i] = buf_load16<SH>(t.k[h], (i * 64 + lane) * 16 - h * Desc::HB);
+    });
+    static_for<0, NLD>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      constexpr int h = Desc::part(i * 1024);
+      vr[i] = buf_load16<SH>(t.v[h], (i * 64 + lane) * 16 - h * Desc::HB);
+    });
   };
   auto consume = [&](auto masked, const u32x4 (&kr)[NLD], const u32x4 (&vr)[NLD], int limit) {
     constexpr bool MASKED = decltype(masked)::value;
@@ -166,21 +173,17 @@ __device__ __forceinline__ void valu_item(const DecodeArgs& a, const int h, cons
   auto pipeline = [&](auto shared) {
     static_for<0, DEPTH - 1>([&](auto dc) {
       constexpr int d = decltype(dc)::value;
-      Rsrc rk, rv;
-      tile(d, id_at(d), lim[d], rk, rv);
-      load(shared, rk, rv, kr[d], vr[d]);
+      load(shared, tile(d, id_at(d), lim[d]), kr[d], vr[d]);
     });
-    int next_id = id_at(DEPTH - 1);
+    TileIds<BS> next_id = id_at(DEPTH - 1);
     for (int k = 0; k < nk; k += DEPTH) {
       static_for<0, DEPTH>([&](auto dc) {
         constexpr int d = decltype(dc)::value;
         constexpr int dn = (d + DEPTH - 1) % DEPTH;
-        const int kn = k + d + DEPTH - 1;  // block whose loads are issued now
-        const int id = next_id;
+        const int kn = k + d + DEPTH - 1;  // tile whose loads are issued now
+        const TileIds<BS> id = next_id;
         next_id = id_at(kn + 1);
-        Rsrc rk, rv;
-        tile(kn, id, lim[dn], rk, rv);
-        load(shared, rk, rv, kr[dn], vr[dn]);
+        load(shared, tile(kn, id, lim[dn]), kr[dn], vr[dn]);
         consume_block(kr[d], vr[d], lim[d]);
       });
     }
@@ -192,7 +195,8 @@ __device__ __forceinline__ void valu_item(const DecodeArgs& a, const int h, cons
     // items stream their tiles non-temporally.
     const int32_t* nb = a.num_seqs > 1 ? a.block_tables +
                             (int64_t)(s > 0 ? s - 1 : s + 1) * a.max_blocks_per_seq : nullptr;
-    if (nb != nullptr && nb[j0] == bt[j0])
+    if (nb != nullptr && tile_ids<BS>(nb, j0, a.max_blocks_per_seq).id[0] ==
+                             tile_ids<BS>(bt, j0, a.max_blocks_per_seq).id[0])
       pipeline(std::true_type{});
     else
       pipeline(std::false_type{});
@@ -271,13 +275,13 @@ __device__ __forceinline__ void valu_item(const DecodeArgs& a, const int h, cons
 // workgroups are dealt to the 8 XCDs round-robin, so the equal-sized items of
 // one (sequence, partition) spread evenly over the XCDs, and one head unit of
 // every sequence stays on one XCD (shared prefix pages then hit its L2).
-template <int DT, int D, int NW, int DEPTH>
+template <int DT, int D, int NW, int DEPTH, int BS>
 __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(DecodeArgs a) {
   __shared__ ValuLds<DT, D, NW> sm;
   const int unit = blockIdx.x, s = longest_first(a, blockIdx.y), part = blockIdx.z;
   const int L = clamp_len(a, s);
   if (part >= parts_of(L, a.part_blocks)) return;  // past this sequence's end
-  valu_item<DT, D, NW, DEPTH, false>(a, unit, s, part, L, &sm);
+  valu_item<DT, D, NW, DEPTH, false, BS>(a, unit, s, part, L, &sm);
 }
 
 // One wave per item: wave w of workgroup z takes partition z * NW + w, for
@@ -304,10 +308,11 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_wave_kernel(DecodeArgs a)
 // waves and 2 tiles in flight, which keeps more workgroups resident per CU.
 constexpr int kLongItemBlocks = 128;
 
-template <int DT, int D, int NW, int DEPTH>
+template <int DT, int D, int NW, int DEPTH, int BS = kBlockSize>
 hipError_t launch_shape(const DecodeArgs& a, hipStream_t stream) {
   const dim3 grid(a.num_q_heads, a.num_seqs, a.max_partitions);
-  hipLaunchKernelGGL((decode_valu_kernel<DT, D, NW, DEPTH>), grid, dim3(NW * 64), 0, stream, a);
+  hipLaunchKernelGGL((decode_valu_kernel<DT, D, NW, DEPTH, BS>), grid, dim3(NW * 64), 0, stream,
+                     a);
   return hipGetLastError();
 }
 
@@ -334,6 +339,13 @@ hipError_t launch_wave_shape(const DecodeArgs& a, hipStream_t stream) {
 
 template <int DT, int D>
 hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
+  // 8- and 32-token blocks: workgroup-per-item kernels for every launch.
+  if (a.block_size == 8)
+    return a.part_blocks >= kLongItemBlocks ? launch_shape<DT, D, 8, 3, 8>(a, stream)
+                                            : launch_shape<DT, D, 4, 2, 8>(a, stream);
+  if (a.block_size == 32)
+    return a.part_blocks >= kLongItemBlocks ? launch_shape<DT, D, 8, 3, 32>(a, stream)
+                                            : launch_shape<DT, D, 4, 2, 32>(a, stream);
   // After a shared-prefix pass the items hold only the private blocks.
   if (a.prefix_blocks != nullptr)
     return launch_shape<DT, D, PA_CASCADE_WAVES, PA_CASCADE_DEPTH>(a, stream);

@@ -20,6 +20,79 @@ __device__ __forceinline__ int parts_of(int L, int part_blocks) {
   return P > 0 ? P : 1;
 }
 
+// Pool blocks of BS-token blocks that hold 16-token tile j of a sequence
+// (tokens 16j .. 16j+15; `bt` is its table row of M entries): one block
+// (BS 16), half of one (BS 32: rows 16 (j % 2) ..), or two (BS 8: the tile's
+// first 8 rows in block bt[2j], the last 8 in bt[2j+1]).  Every kernel works
+// on 16-token tiles; only this mapping and the descriptors below see BS.
+template <int BS>
+struct TileIds {
+  static_assert(BS == 8 || BS == 16 || BS == 32, "block size");
+  static constexpr int H = BS == 8 ? 2 : 1;  // blocks per tile
+  int id[H];
+};
+
+template <int BS>
+__device__ __forceinline__ TileIds<BS> tile_ids(const int32_t* bt, int j, int M) {
+  TileIds<BS> t;
+  if constexpr (BS == 16) {
+    t.id[0] = bt[j];
+  } else if constexpr (BS == 32) {
+    t.id[0] = bt[j >> 1];
+  } else {
+    t.id[0] = bt[2 * j];
+    t.id[1] = bt[min(2 * j + 1, M - 1)];  // past the context when clamped: masked
+  }
+  return t;
+}
+
+// Buffer descriptors of one 16-token tile of one KV head in both caches,
+// one per block it spans; empty (zero records: loads return zeros, touch
+// nothing) for a tile past the item's end or a block id outside the pool.
+// TB = bytes of a 16-row tile.
+template <int BS, int TB>
+struct TileDesc {
+  static constexpr int H = TileIds<BS>::H;
+  static constexpr int HB = TB / H;  // bytes per block part
+  Rsrc k[H], v[H];
+  // Part and offset of byte `off` of the tile (off known at compile time
+  // per load, so the part is too).
+  static constexpr int part(int off) { return off / HB; }
+};
+
+template <int BS, int TB>
+__device__ __forceinline__ TileDesc<BS, TB> tile_desc(const DecodeArgs& a, const TileIds<BS>& ids,
+                                                      int j, int kvh, bool ok) {
+  TileDesc<BS, TB> d;
+  const char* kc = static_cast<const char*>(a.k_cache);
+  const char* vc = static_cast<const char*>(a.v_cache);
+#pragma unroll
+  for (int h = 0; h < TileIds<BS>::H; ++h) {
+    const bool okh = ok && (uint32_t)ids.id[h] < (uint32_t)a.num_blocks_i32;
+    const int64_t bid = okh ? ids.id[h] : 0;
+    int64_t off;
+    if constexpr (BS == 32)
+      off = (bid * a.num_kv_heads + kvh) * (2 * TB) + (j & 1) * TB;
+    else
+      off = (bid * a.num_kv_heads + kvh) * TileDesc<BS, TB>::HB;
+    d.k[h] = make_rsrc(kc + off, okh ? TileDesc<BS, TB>::HB : 0);
+    d.v[h] = make_rsrc(vc + off, okh ? TileDesc<BS, TB>::HB : 0);
+  }
+  return d;
+}
+
+// Tokens of a 16-token tile that count (`left` = context tokens from the
+// tile's first on): tokens in a block whose id lies outside the pool do not.
+template <int BS>
+__device__ __forceinline__ int tile_limit(const DecodeArgs& a, const TileIds<BS>& ids, int left) {
+  int n = min(kBlockSize, left);
+  if ((uint32_t)ids.id[0] >= (uint32_t)a.num_blocks_i32) return 0;
+  if constexpr (BS == 8) {
+    if ((uint32_t)ids.id[1] >= (uint32_t)a.num_blocks_i32) n = min(n, 8);
+  }
+  return n;
+}
+
 // Sequence that grid slot `slot` works on.  The hardware dispatcher starts
 // workgroups in grid order, so slots take the sequences in decreasing order
 // of context length (ties by index): the longest items start first and the

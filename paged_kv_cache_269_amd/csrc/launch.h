@@ -26,6 +26,8 @@ struct DecodeArgs {
   int part_blocks;              // blocks per partition
   int max_partitions;           // P (partials stride)
   float scale_log2;             // scale * log2(e)
+  int block_size;               // tokens per pool block: 8, 16 or 32 (kernels work on
+                                // 16-token tiles; lengths and partitions count those)
   // Shared-prefix launches: per sequence, the leading blocks whose attention
   // the prefix kernel has already computed (nullptr: none), and that part's
   // state per (sequence, query head) row.
@@ -58,7 +60,7 @@ struct ReduceArgs {
 
 hipError_t launch_reshape_and_cache(const void* key, const void* value, void* k_cache,
                                     void* v_cache, const int64_t* slot_mapping, int num_tokens,
-                                    int num_kv_heads, int head_dim, int elem_bytes,
+                                    int num_kv_heads, int head_dim, int elem_bytes, int block_size,
                                     int64_t num_blocks, hipStream_t stream);
 
 // Block copies inside both caches: pairs [num_pairs, 2] int32 (src, dst) on

@@ -32,6 +32,7 @@
 #include <type_traits>
 
 #include "common.h"
+#include "items.h"
 #include "launch.h"
 
 namespace pa {
@@ -131,34 +132,30 @@ struct MfmaState {
   }
 };
 
-// Descriptors of the tile of pool block `bid` for KV head kvh; empty when
-// !ok (loads through them return zeros without touching memory).
-template <int DT, int D>
-__device__ __forceinline__ void tile_rsrc(const DecodeArgs& a, int bid, int kvh, bool ok, Rsrc& rk,
-                                          Rsrc& rv) {
-  using S = MfmaShape<DT, D>;
-  ok = ok && (uint32_t)bid < (uint32_t)a.num_blocks_i32;
-  const int64_t off = ((int64_t)(ok ? bid : 0) * a.num_kv_heads + kvh) * S::TILE_BYTES;
-  rk = make_rsrc(static_cast<const char*>(a.k_cache) + off, ok ? S::TILE_BYTES : 0);
-  rv = make_rsrc(static_cast<const char*>(a.v_cache) + off, ok ? S::TILE_BYTES : 0);
-}
-
-// The lane's share of one tile.  K: load jj is the tile's jj-th contiguous
-// KiB (lane l takes its 16-byte chunk l), so every load reads whole cache
-// lines; the rows reach the matrix-core layout through LDS (stage_k).  V:
-// rows g + 4e, already in the P.V operand layout.
-template <int DT, int D, bool SH>
-__device__ __forceinline__ void load_tile(Rsrc rk, Rsrc rv, const MfmaLane& ln,
+// The lane's share of one 16-token tile.  K: load jj is the tile's jj-th
+// contiguous KiB (lane l takes its 16-byte chunk l), so every load reads
+// whole cache lines; the rows reach the matrix-core layout through LDS
+// (stage_k).  V: rows g + 4e, already in the P.V operand layout.  Which
+// block part a load reads is known per load at compile time.
+template <int DT, int D, bool SH, int BS, int TB>
+__device__ __forceinline__ void load_tile(const TileDesc<BS, TB>& t, const MfmaLane& ln,
                                           u32x4 (&kr)[D / 32],
                                           typename MfmaShape<DT, D>::VT (&vr)[4]) {
   using S = MfmaShape<DT, D>;
+  using Desc = TileDesc<BS, TB>;
+  static_assert(TB == S::TILE_BYTES, "tile bytes");
   const int lane = ln.n + 16 * ln.g;
-#pragma unroll
-  for (int jj = 0; jj < S::NJ; ++jj) kr[jj] = buf_load16<SH>(rk, (jj * 64 + lane) * 16);
-#pragma unroll
-  for (int e = 0; e < 4; ++e)
-    vr[e] = S::VS::template load<SH>(rv, ((ln.g + 4 * e) * 16 + ln.n) *
-                                             (int)sizeof(typename S::VT));
+  static_for<0, S::NJ>([&](auto jc) {
+    constexpr int jj = decltype(jc)::value;
+    constexpr int h = Desc::part(jj * 1024);
+    kr[jj] = buf_load16<SH>(t.k[h], (jj * 64 + lane) * 16 - h * Desc::HB);
+  });
+  static_for<0, 4>([&](auto ec) {
+    constexpr int e = decltype(ec)::value;
+    constexpr int h = Desc::part(4 * e * S::CPR * 16);  // rows 4e .. 4e+3
+    vr[e] = S::VS::template load<SH>(t.v[h], ((ln.g + 4 * e) * 16 + ln.n) *
+                                                 (int)sizeof(typename S::VT) - h * Desc::HB);
+  });
 }
 
 // Force the wait for registers just loaded (an empty asm reading them).

@@ -122,9 +122,9 @@ __global__ __launch_bounds__(NW * 64) void prefix_kernel(DecodeArgs a, PrefixOut
   auto issue = [&](int kk, int bid, int slot) {
     const bool ok = kk < nk && (uint32_t)bid < (uint32_t)a.num_blocks_i32;
     lim[slot] = ok ? kBlockSize : 0;
-    Rsrc rk, rv;
-    tile_rsrc<DT, D>(a, bid, kvh, ok, rk, rv);
-    load_tile<DT, D, true>(rk, rv, ln, kr[slot], vr[slot]);
+    load_tile<DT, D, true>(tile_desc<kBlockSize, S::TILE_BYTES>(a, TileIds<kBlockSize>{{bid}},
+                                                                w + kk * NW, kvh, ok),
+                           ln, kr[slot], vr[slot]);
   };
   if (nk > 0) {
     static_for<0, DEPTH - 1>([&](auto dc) {

@@ -163,11 +163,15 @@ def _draw_lengths(rng: np.random.Generator, p: dict) -> np.ndarray:
         lens = np.clip(np.rint(np.exp(x)), 1, p["len_cap"]).astype(np.int64)
     else:
         raise ValueError(f"unknown length distribution {dist!r}")
-    return lens.astype(np.int64) + BLOCK_SIZE * p.get("shared_prefix_blocks", 0)
+    return lens.astype(np.int64) + _bs(p) * p.get("shared_prefix_blocks", 0)
+
+
+def _bs(p: dict) -> int:
+    return int(p.get("block_size", BLOCK_SIZE))
 
 
 def _len_cap(p: dict) -> int:
-    prefix = BLOCK_SIZE * p.get("shared_prefix_blocks", 0)
+    prefix = _bs(p) * p.get("shared_prefix_blocks", 0)
     if p["len_dist"] == "fixed":
         return int(max(p["lens"])) + prefix
     if p["len_dist"] == "uniform":
@@ -197,13 +201,14 @@ def generate(name: str, poison: bool = True, threads: Optional[int] = None,
     if Hq % Hkv:
         raise ValueError("num_q_heads must be a multiple of num_kv_heads")
     shared = int(p.get("shared_prefix_blocks", 0))
+    bs = int(p.get("block_size", BLOCK_SIZE))
     root = np.random.SeedSequence(p["seed"])
     s_len, s_perm, s_q, s_k, s_v, s_nk, s_nv = root.spawn(7)
 
     lens = _draw_lengths(np.random.default_rng(s_len), p)
-    if shared and np.any(lens <= BLOCK_SIZE * shared):
+    if shared and np.any(lens <= bs * shared):
         raise ValueError("shared-prefix sequences need a private suffix")
-    pages = (lens + BLOCK_SIZE - 1) // BLOCK_SIZE
+    pages = (lens + bs - 1) // bs
     private_pages = pages - shared
     needed = int(shared + private_pages.sum())
     if "pool_blocks" in p:
@@ -212,7 +217,7 @@ def generate(name: str, poison: bool = True, threads: Optional[int] = None,
             raise ValueError("pool too small for the drawn lengths")
     else:
         N = int(math.ceil(1.2 * needed))
-    M = max(1, (_len_cap(p) + BLOCK_SIZE - 1) // BLOCK_SIZE)
+    M = max(1, (_len_cap(p) + bs - 1) // bs)
     if int(pages.max(initial=0)) > M:
         raise ValueError("a drawn length exceeds the block-table row")
 
@@ -229,13 +234,13 @@ def generate(name: str, poison: bool = True, threads: Optional[int] = None,
     # newest token of each sequence sits at logical position L-1; an empty
     # sequence writes nothing (slot -1)
     last = np.maximum(lens - 1, 0)
-    slots = (tables[np.arange(B), last // BLOCK_SIZE].astype(np.int64) * BLOCK_SIZE
-             + last % BLOCK_SIZE).astype(np.int64)
+    slots = (tables[np.arange(B), last // bs].astype(np.int64) * bs
+             + last % bs).astype(np.int64)
     slots[lens == 0] = -1
 
     q = _normal(s_q, (B, Hq, D), dtype)
-    k_cache = _normal_pool(s_k, (N, Hkv, BLOCK_SIZE, D), dtype, threads=threads)
-    v_cache = _normal_pool(s_v, (N, Hkv, BLOCK_SIZE, D), dtype, threads=threads)
+    k_cache = _normal_pool(s_k, (N, Hkv, bs, D), dtype, threads=threads)
+    v_cache = _normal_pool(s_v, (N, Hkv, bs, D), dtype, threads=threads)
     key = _normal(s_nk, (B, Hkv, D), dtype)
     value = _normal(s_nv, (B, Hkv, D), dtype)
 
@@ -245,15 +250,15 @@ def generate(name: str, poison: bool = True, threads: Optional[int] = None,
         for cache in (k_cache, v_cache):
             _nan_fill(cache, dtype, ~used)
             for s in range(B):
-                tail = int(lens[s] % BLOCK_SIZE)
+                tail = int(lens[s] % bs)
                 if tail:
                     _nan_fill(cache, dtype, (tables[s, pages[s] - 1], slice(None), slice(tail, None)))
             w_ = slots[slots >= 0]
-            _nan_fill(cache, dtype, (w_ // BLOCK_SIZE, slice(None), w_ % BLOCK_SIZE))
+            _nan_fill(cache, dtype, (w_ // bs, slice(None), w_ % bs))
 
     scale = float(p.get("scale", 1.0 / math.sqrt(D)))
     return Workload(name=name, dtype=dtype, num_seqs=B, num_q_heads=Hq, num_kv_heads=Hkv,
-                    head_dim=D, block_size=BLOCK_SIZE, num_blocks=N, max_blocks_per_seq=M,
+                    head_dim=D, block_size=bs, num_blocks=N, max_blocks_per_seq=M,
                     scale=scale, partition_size=int(p.get("partition_size", 512)),
                     shared_prefix_blocks=shared, context_lens=lens.astype(np.int32),
                     block_tables=tables, slot_mapping=slots, q=q, key=key, value=value,
@@ -284,13 +289,13 @@ def algorithmic_bytes(w: Workload, unique: bool = True) -> Dict[str, int]:
     lens = w.context_lens.astype(np.int64)
     total_tokens = int(lens.sum())
     if unique and w.shared_prefix_blocks:
-        prefix = BLOCK_SIZE * w.shared_prefix_blocks
+        prefix = w.block_size * w.shared_prefix_blocks
         kv_tokens = prefix + int((lens - prefix).sum())
     else:
         kv_tokens = total_tokens
     kv = kv_tokens * per_tok
     qo = 2 * w.num_seqs * w.num_q_heads * w.head_dim * e
-    pages = int(((lens + BLOCK_SIZE - 1) // BLOCK_SIZE).sum())
+    pages = int(((lens + w.block_size - 1) // w.block_size).sum())
     meta = 4 * pages + 4 * w.num_seqs
     return dict(kv=kv, q_out=qo, meta=meta, total=kv + qo + meta,
                 logical_kv=total_tokens * per_tok)

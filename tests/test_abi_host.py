@@ -56,7 +56,8 @@ def test_decode_argument_checks(hiplib):
     assert _decode(lib, out=None) == NULL
     assert _decode(lib, bt=None) == NULL
     assert _decode(lib, D=96) == UNSUP
-    assert _decode(lib, bs=32) == UNSUP
+    assert _decode(lib, bs=24) == UNSUP     # 8, 16 and 32 are the block sizes taken
+    assert _decode(lib, bs=64) == UNSUP
     assert _decode(lib, dtype=7) == UNSUP
     assert _decode(lib, part=100) == UNSUP
     assert _decode(lib, part=-16) == UNSUP
@@ -118,7 +119,7 @@ def test_reshape_and_reduce_argument_checks(hiplib):
     r = lib.pa_reshape_and_cache
     assert r(None, FAKE, FAKE, FAKE, FAKE, 3, 2, 128, 16, 10, 2, None) == NULL
     assert r(FAKE, FAKE, FAKE, FAKE, FAKE, 3, 2, 80, 16, 10, 2, None) == UNSUP
-    assert r(FAKE, FAKE, FAKE, FAKE, FAKE, 3, 2, 128, 8, 10, 2, None) == UNSUP
+    assert r(FAKE, FAKE, FAKE, FAKE, FAKE, 3, 2, 128, 12, 10, 2, None) == UNSUP
     assert r(FAKE, FAKE, FAKE, FAKE, FAKE, -3, 2, 128, 16, 10, 2, None) == SHAPE
     assert r(None, None, None, None, None, 0, 2, 128, 16, 10, 2, None) == OK
     d = lib.pa_paged_attention_reduce

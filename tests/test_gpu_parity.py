@@ -194,3 +194,49 @@ def test_reshape_padding_and_out_of_pool_slots_are_skipped(cuda):
     slots_oracle[3] = -1
     oracle.reshape_and_cache(w.key, w.value, w.k_cache, w.v_cache, slots_oracle, w.dtype)
     pool_equal(run, w)
+
+
+@pytest.mark.parametrize("bs", [8, 32])
+@pytest.mark.parametrize("dtype,D,G", [("bf16", 128, 1), ("f16", 64, 1), ("f32", 128, 1),
+                                        ("bf16", 128, 8), ("f16", 64, 4), ("bf16", 128, 3)])
+def test_block_sizes_8_and_32(cuda, bs, dtype, D, G):
+    """Pool blocks of 8 and 32 tokens ([DM] block-size notes): KV write
+    placement bit-exact, decode within tolerance for the edge lengths, one
+    pass and 16/512-token partitions (the kernels work on 16-token tiles: a
+    tile is two 8-token blocks or half of a 32-token block)."""
+    Hkv = 2
+    announce("block size", bs, dtype, D, G)
+    w = W.generate("long_context", dtype=dtype, head_dim=D, num_kv_heads=Hkv,
+                   num_q_heads=Hkv * G, lens=EDGE_LENS, seed=78, block_size=bs)
+    run = Run(w, cuda)
+    run.reshape()
+    run.oracle_reshape()
+    pool_equal(run, w)
+    ref = full_oracle(w)
+    for part in (0, 16, 512):
+        got_raw = tensor_to_np(run.decode(partition_size=part), dtype)
+        got = to_f64(got_raw, dtype)
+        check_close(got, ref, dtype, f"bs {bs} {dtype} D{D} G{G} partition {part}")
+        assert not got[EDGE_LENS.index(0)].any()
+        s1 = EDGE_LENS.index(1)
+        for h in range(w.num_q_heads):
+            assert np.array_equal(got_raw[s1, h], w.value[s1, h // G]), "L=1 not exact"
+
+
+@pytest.mark.parametrize("bs", [8, 32])
+def test_block_sizes_full_llama7b_shape(cuda, bs):
+    """The LLaMA-7B-shape workload laid out in 8- or 32-token blocks, sampled
+    rows against the oracle (the launch the block-size measurement times)."""
+    announce("block size full", bs)
+    w = W.generate("llama7b", block_size=bs)
+    run = Run(w, cuda)
+    run.reshape()
+    out = tensor_to_np(run.decode(), w.dtype)
+    run.oracle_reshape()
+    pool_equal(run, w)
+    rng = np.random.default_rng(bs)
+    B, Hq = w.num_seqs, w.num_q_heads
+    flat = rng.choice(B * Hq, size=64, replace=False)
+    seqs, heads = flat // Hq, flat % Hq
+    ref = oracle_rows(w, list(seqs), list(heads))
+    check_close(to_f64(out[seqs, heads], w.dtype), ref, w.dtype, f"llama7b bs {bs}")
