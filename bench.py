@@ -57,6 +57,9 @@ def parse_args(argv=None):
     ap.add_argument("--block-ops", action="store_true",
                     help="also time pa_copy_blocks (device) and pa_swap_blocks (device <-> "
                          "pinned host) on blocks of this workload's pool")
+    ap.add_argument("--query-len", type=int, default=0,
+                    help="also time pa_paged_attention_multi_query with this many new query "
+                         "tokens per sequence (causal over each context's last tokens)")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB before warmup, as the "
                          "known-size reference for HBM byte counters")
@@ -301,6 +304,59 @@ def block_ops(w, dev):
                     "one asynchronous copy each"}
 
 
+def multi_query_bench(args, w, d, pools, part, stream):
+    """The multi-query entry point on this workload's pool: every sequence's
+    last ``args.query_len`` context tokens as queries.  Algorithmic bytes: K/V
+    of every context token once, q in, out, the table entries and offsets;
+    re-reads of a tile by the 16-row units of one KV head are overhead."""
+    import numpy as np
+    import torch
+    import paged_kv_cache_269_amd as pa
+    from paged_kv_cache_269_amd import workloads as W
+
+    spans = W.generate_query_spans(w, args.query_len, seed=7)
+    T = spans.num_tokens
+    tdt = W.torch_dtype(w.dtype)
+    q = torch.from_numpy(spans.q)
+    q = (q.view(torch.bfloat16) if w.dtype == "bf16" else q).to(d["q"].device)
+    qs = torch.from_numpy(spans.query_start).to(q.device)
+    out = torch.empty_like(q)
+    assert out.dtype == tdt
+    ws = pa.multi_query_workspace(T, w.num_q_heads, w.head_dim, w.max_context_len, part,
+                                  device=q.device)
+
+    def call(i):
+        kc, vc = pools[i % len(pools)]
+        pa.paged_attention_multi_query(out, q, kc, vc, d["block_tables"], d["context_lens"], qs,
+                                       w.scale, w.max_context_len, spans.max_query_len,
+                                       partition_size=part, workspace=ws, stream=stream)
+
+    for i in range(max(3, args.warmup)):
+        call(i)
+    torch.cuda.synchronize()
+    K = max(10, args.steps)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(K)]
+    for i in range(K):
+        ev[i][0].record(stream)
+        call(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    us = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3
+    ab = W.algorithmic_bytes(w, unique=True)
+    qo = 2 * T * w.num_q_heads * w.head_dim * w.elem_bytes
+    nbytes = ab["kv"] + qo + ab["meta"] + 4 * (w.num_seqs + 1)
+    flops = W.multi_query_flops(w, spans)
+    gbps = nbytes / us / 1e3
+    tflops = flops / us / 1e6
+    return {"entry": "pa_paged_attention_multi_query", "query_len": args.query_len,
+            "query_tokens": T, "partition_size": part, "launch_us_avg": round(us, 2),
+            "algorithmic_bytes": nbytes, "GBps": round(gbps, 1),
+            "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4), "flops": flops,
+            "TFLOPs": round(tflops, 2), "frac_mfma_peak": round(tflops / 2500.0, 5),
+            "tokens_per_s": round(T / us * 1e6, 1)}
+
+
 def main(argv=None) -> int:
     args = parse_args(argv)
     if args.gpus != 1:
@@ -430,6 +486,8 @@ def main(argv=None) -> int:
                      "launch_us_p90": round(float(np.percentile(dec_ms, 90)) * 1e3, 2),
                      "algorithmic_bytes_per_launch": ab["total"]},
     }
+    if args.query_len > 0:
+        result["multi_query"] = multi_query_bench(args, w, d, pools, part, stream)
     if args.block_ops:
         result["block_ops"] = block_ops(w, dev)
     if args.loop_steps > 0:

@@ -194,6 +194,67 @@ int pa_paged_attention_decode_cascade(void* out, const void* q, const void* k_ca
 size_t pa_cascade_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim);
 
 /*
+ * Multi-token queries over the paged cache: several new tokens per sequence
+ * in one call (chunked prefill; checking drafted tokens in one forward pass,
+ * [CX] §4.1; variable-length attention with per-sequence query offsets,
+ * [DM] FlashAttention backend).  Sequence s owns query tokens
+ * query_start[s] <= t < query_start[s + 1] (n_s of them, the last n_s
+ * tokens of its context, their K/V already written by
+ * pa_reshape_and_cache).  Token i of the span sits at position
+ * p = L - n_s + i (L = context_lens[s], clamped as in decode) and attends to
+ * tokens 0 .. p:
+ *     out[t,h,:] = sum_{u<=p} softmax_u(scale * q[t,h,:] . k_u) v_u,
+ * which is [CX] §1.1's o_t = Attention(q_t, K_{1:t}, V_{1:t}) for every new
+ * token at once.  A token with p < 0 gets a zero row; n_s = 1 is decode.
+ *
+ * Layouts: q, out [num_query_tokens, num_q_heads, head_dim];
+ * query_start [num_seqs + 1] int32 device array, query_start[0] = 0,
+ * non-decreasing, query_start[num_seqs] = num_query_tokens (rows of tokens
+ * that no sequence's span covers are left undefined);
+ * caches, block_tables, context_lens as for decode.  max_query_len bounds
+ * every n_s (the kernels take at most that many tokens of a span; the rest
+ * of it is left undefined).  pa_validate_query_start_host checks a host copy.
+ *
+ * dtype PA_F16 or PA_BF16 (PA_F32: PA_ERR_UNSUPPORTED).  partition_size as
+ * for decode (0: one partition); with more than one partition `workspace`
+ * must hold pa_multi_query_workspace_bytes(...) bytes (partials as in
+ * decode with one row per (query token, head), and each token's causal
+ * length).  num_seqs, num_query_tokens <= 65535.  Errors as for decode;
+ * num_seqs, num_query_tokens or max_query_len = 0 is a no-op.
+ */
+int pa_paged_attention_multi_query(void* out, const void* q, const void* k_cache,
+                                   const void* v_cache, const int32_t* block_tables,
+                                   const int32_t* context_lens, const int32_t* query_start,
+                                   int32_t num_seqs, int32_t num_query_tokens,
+                                   int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                   int32_t block_size, int32_t max_blocks_per_seq,
+                                   int64_t num_blocks, float scale, int32_t dtype,
+                                   int32_t max_query_len, int32_t partition_size,
+                                   int32_t max_context_len, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+
+/*
+ * Workspace bytes of pa_paged_attention_multi_query: 0 when every token
+ * fits one partition (partition_size = 0 or max_context_len <=
+ * partition_size), else the decode partials for num_query_tokens rows plus
+ * one int32 per query token.  Returns 0 for invalid arguments.
+ */
+size_t pa_multi_query_workspace_bytes(int32_t num_query_tokens, int32_t num_q_heads,
+                                      int32_t head_dim, int32_t max_context_len,
+                                      int32_t partition_size);
+
+/*
+ * Host-side check of query offsets (host pointers): query_start[0] = 0,
+ * query_start[num_seqs] = num_query_tokens, every span length n_s in
+ * [0, max_query_len] and, when context_lens is not NULL, n_s <=
+ * context_lens[s].  Returns PA_OK, PA_ERR_RANGE, PA_ERR_NULL or PA_ERR_SHAPE.
+ * Touches no GPU.
+ */
+int pa_validate_query_start_host(const int32_t* query_start, const int32_t* context_lens,
+                                 int32_t num_seqs, int32_t num_query_tokens,
+                                 int32_t max_query_len);
+
+/*
  * Copy-on-write of shared blocks ([CX] §2.1: requests of one prompt --
  * parallel sampling, beam search -- share its pages; [DM] sharing
  * mechanism): for every pair i, block block_pairs[2i] of both caches (all

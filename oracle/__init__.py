@@ -12,7 +12,9 @@ Definitions followed (page titles and sections, see ``oracle.c``):
   * 16-token pages, page table, shared pages -- same page, §2.1;
   * cache layout [num_pages, num_heads, page_size, head_dim] and the token
     address page_id * BLOCK_SIZE + page_offset -- same page, §2.2;
-  * gather through the block table -- vLLM tutorial (mjmagnets.cn), §2.2.
+  * gather through the block table -- vLLM tutorial (mjmagnets.cn), §2.2;
+  * several new query tokens per sequence, each attending causally to the
+    context up to its own position -- the §1.1 definition for each of them.
 """
 from __future__ import annotations
 
@@ -177,3 +179,41 @@ def lse_merge(m, l, o, num_parts) -> np.ndarray:
     rc = _load().oracle_lse_merge(_ptr(out), _ptr(m), _ptr(l), _ptr(o), _ptr(np_), R, P, D)
     _check("oracle_lse_merge", rc)
     return out
+
+
+def multi_query(q, k_cache, v_cache, block_tables, context_lens, query_start, scale: float,
+                dtype: str, rows_token: Optional[Sequence[int]] = None,
+                rows_head: Optional[Sequence[int]] = None, num_threads: int = 0) -> np.ndarray:
+    """Several new query tokens per sequence: out [T, Hq, D] float64.
+
+    Sequence s owns query tokens query_start[s] .. query_start[s+1] - 1, the
+    last n_s of its L_s context tokens; token i of that span sits at position
+    p = L_s - n_s + i and attends to tokens 0 .. p.  That is the decode
+    definition o_t = Attention(q_t, K_{1:t}, V_{1:t}) ("vLLM 2026 推理引擎全解"
+    (chenxutan.com) §1.1) once for each of those t, so every row here is one
+    decode row of oracle.c over the token range [0, p + 1); a token with
+    p < 0 gets a zero row.  q [T, Hq, D].  With ``rows_token``/``rows_head``
+    only those (token, head) rows are computed and [R, D] is returned.
+    """
+    q = _c(q)
+    qs = _c(query_start, np.int64)
+    bt, cl = _c(block_tables, np.int32), _c(context_lens, np.int32)
+    T, Hq, D = q.shape
+    B = qs.shape[0] - 1
+    if qs[0] != 0 or qs[-1] != T or (np.diff(qs) < 0).any() or cl.shape[0] != B:
+        raise ValueError("query_start must run from 0 to T without decreasing")
+    n = np.diff(qs)
+    seq_of = np.repeat(np.arange(B), n)                      # sequence of each query token
+    pos = cl[seq_of].astype(np.int64) - n[seq_of] + (np.arange(T) - qs[seq_of])
+    full = rows_token is None
+    if full:
+        rows_tok = np.repeat(np.arange(T, dtype=np.int32), Hq)
+        rows_h = np.tile(np.arange(Hq, dtype=np.int32), T)
+    else:
+        rows_tok, rows_h = _c(rows_token, np.int32), _c(rows_head, np.int32)
+    t_end = np.maximum(pos[rows_tok] + 1, 0).astype(np.int32)
+    # one "sequence" per query token: its q row, its sequence's table and length
+    out, _, _ = decode_rows(q, k_cache, v_cache, bt[seq_of], cl[seq_of], scale, dtype,
+                            rows_tok, rows_h, np.zeros_like(t_end), t_end,
+                            num_threads=num_threads)
+    return out.reshape(T, Hq, D) if full else out

@@ -17,13 +17,17 @@ from ._binding import (  # noqa: F401
     decode_workspace_bytes,
     lib_path,
     load_library,
+    multi_query_workspace,
+    multi_query_workspace_bytes,
     paged_attention_decode,
     paged_attention_decode_cascade,
+    paged_attention_multi_query,
     paged_attention_reduce,
     reshape_and_cache,
     status_string,
     swap_blocks,
     validate_copy_host,
+    validate_query_start_host,
     validate_slots_host,
     validate_tables_host,
     version,
@@ -33,7 +37,9 @@ from ._binding import (  # noqa: F401
 __all__ = [
     "BlockManager", "KVCacheExhausted", "PagedAttnError", "cascade_workspace",
     "cascade_workspace_bytes", "copy_blocks", "decode_workspace", "decode_workspace_bytes",
-    "lib_path", "load_library", "paged_attention_decode", "paged_attention_decode_cascade",
+    "lib_path", "load_library", "multi_query_workspace", "multi_query_workspace_bytes",
+    "paged_attention_decode", "paged_attention_decode_cascade", "paged_attention_multi_query",
     "paged_attention_reduce", "reshape_and_cache", "status_string", "swap_blocks",
-    "validate_copy_host", "validate_slots_host", "validate_tables_host", "version", "EXPORTS",
+    "validate_copy_host", "validate_query_start_host", "validate_slots_host",
+    "validate_tables_host", "version", "EXPORTS",
 ]

@@ -39,6 +39,11 @@ EXPORTS = {
                                                          _I32, _I32, _I32, _I32, _I64, _F32,
                                                          _I32, _I32, _P, _SZ, _P]),
     "pa_cascade_workspace_bytes": (ctypes.c_size_t, [_I32, _I32, _I32]),
+    "pa_paged_attention_multi_query": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I32, _I32,
+                                                      _I32, _I32, _I32, _I32, _I32, _I64, _F32,
+                                                      _I32, _I32, _I32, _I32, _P, _SZ, _P]),
+    "pa_multi_query_workspace_bytes": (ctypes.c_size_t, [_I32, _I32, _I32, _I32, _I32]),
+    "pa_validate_query_start_host": (ctypes.c_int, [_P, _P, _I32, _I32, _I32]),
     "pa_validate_tables_host": (ctypes.c_int, [_P, _P, _I32, _I32, _I64, _I32]),
     "pa_validate_slots_host": (ctypes.c_int, [_P, _I32, _I64, _I32]),
     "pa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -226,6 +231,69 @@ def paged_attention_decode_cascade(out, q, k_cache, v_cache, block_tables, conte
         _dev_ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
         _stream_handle(stream))
     _check("pa_paged_attention_decode_cascade", rc)
+
+
+def multi_query_workspace_bytes(num_query_tokens: int, num_q_heads: int, head_dim: int,
+                                max_context_len: int, partition_size: int) -> int:
+    return int(load_library().pa_multi_query_workspace_bytes(
+        num_query_tokens, num_q_heads, head_dim, max_context_len, partition_size))
+
+
+def multi_query_workspace(num_query_tokens: int, num_q_heads: int, head_dim: int,
+                          max_context_len: int, partition_size: int, device="cuda"):
+    """A uint8 workspace tensor for paged_attention_multi_query (None when
+    none is needed)."""
+    import torch
+    n = multi_query_workspace_bytes(num_query_tokens, num_q_heads, head_dim, max_context_len,
+                                    partition_size)
+    return torch.empty(n, dtype=torch.uint8, device=device) if n else None
+
+
+def paged_attention_multi_query(out, q, k_cache, v_cache, block_tables, context_lens,
+                                query_start, scale: float, max_context_len: int,
+                                max_query_len: int, partition_size: int = 512, workspace=None,
+                                stream=None) -> None:
+    """Causal attention of several new tokens per sequence into ``out``
+    [T, Hq, D]: sequence s owns query rows query_start[s] .. query_start[s+1]-1
+    (int32 device tensor [B + 1]), the last tokens of its context.
+    ``workspace``: at least multi_query_workspace_bytes(...) bytes; allocated
+    here when needed and omitted."""
+    import torch
+    T, Hq, D = q.shape
+    N, Hkv, bs, D2 = k_cache.shape
+    B = context_lens.shape[0]
+    if out.shape != q.shape or D2 != D or v_cache.shape != k_cache.shape:
+        raise ValueError("shape mismatch between q, out and the caches")
+    if not (q.dtype == out.dtype == k_cache.dtype == v_cache.dtype):
+        raise TypeError("q, out and caches must share one element type")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.dim() != 1:
+        raise ValueError("block_tables must be [num_seqs, max_blocks], context_lens [num_seqs]")
+    if query_start.shape != (B + 1,):
+        raise ValueError("query_start must be [num_seqs + 1]")
+    if workspace is None:
+        workspace = multi_query_workspace(T, Hq, D, max_context_len, partition_size, q.device)
+    ws_ptr = _dev_ptr(workspace, "workspace") if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    rc = load_library().pa_paged_attention_multi_query(
+        _dev_ptr(out, "out"), _dev_ptr(q, "q"), _dev_ptr(k_cache, "k_cache"),
+        _dev_ptr(v_cache, "v_cache"), _dev_ptr(block_tables, "block_tables", torch.int32),
+        _dev_ptr(context_lens, "context_lens", torch.int32),
+        _dev_ptr(query_start, "query_start", torch.int32), B, T, Hq, Hkv, D, bs,
+        block_tables.shape[1], N, float(scale), _dtype_code(q), int(max_query_len),
+        int(partition_size), int(max_context_len), ws_ptr, ws_bytes, _stream_handle(stream))
+    _check("pa_paged_attention_multi_query", rc)
+
+
+def validate_query_start_host(query_start, context_lens, num_query_tokens: int,
+                              max_query_len: int) -> int:
+    """Host check of query offsets (numpy/host arrays); returns the status code."""
+    import numpy as np
+    qs = np.ascontiguousarray(query_start, dtype=np.int32)
+    cl = None if context_lens is None else np.ascontiguousarray(context_lens, dtype=np.int32)
+    return int(load_library().pa_validate_query_start_host(
+        qs.ctypes.data_as(ctypes.c_void_p),
+        None if cl is None else cl.ctypes.data_as(ctypes.c_void_p),
+        qs.shape[0] - 1, int(num_query_tokens), int(max_query_len)))
 
 
 def paged_attention_reduce(out, max_logits, exp_sums, tmp_out, context_lens,

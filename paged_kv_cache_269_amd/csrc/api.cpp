@@ -258,6 +258,127 @@ int pa_paged_attention_decode_cascade(void* out, const void* q, const void* k_ca
                      dtype, 0, max_context_len, workspace, workspace_bytes, stream, true);
 }
 
+size_t pa_multi_query_workspace_bytes(int32_t num_query_tokens, int32_t num_q_heads,
+                                      int32_t head_dim, int32_t max_context_len,
+                                      int32_t partition_size) {
+  if (num_query_tokens < 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len < 0 ||
+      partition_size < 0)
+    return 0;
+  const int64_t parts = partition_size ? ceil_div(max_context_len, partition_size) : 1;
+  const WsLayout w = ws_layout(num_query_tokens, num_q_heads, head_dim, parts);
+  return w.total ? w.total + align256((size_t)num_query_tokens * sizeof(int32_t)) : 0;
+}
+
+int pa_paged_attention_multi_query(void* out, const void* q, const void* k_cache,
+                                   const void* v_cache, const int32_t* block_tables,
+                                   const int32_t* context_lens, const int32_t* query_start,
+                                   int32_t num_seqs, int32_t num_query_tokens,
+                                   int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                   int32_t block_size, int32_t max_blocks_per_seq,
+                                   int64_t num_blocks, float scale, int32_t dtype,
+                                   int32_t max_query_len, int32_t partition_size,
+                                   int32_t max_context_len, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  if ((dtype != PA_F16 && dtype != PA_BF16) || !block_size_ok(block_size) ||
+      !head_dim_ok(head_dim))
+    return PA_ERR_UNSUPPORTED;
+  if (partition_size < 0 || partition_size % kBlock) return PA_ERR_UNSUPPORTED;
+  if (num_seqs < 0 || num_seqs > kMaxGridYZ || num_query_tokens < 0 ||
+      num_query_tokens > kMaxGridYZ || num_q_heads <= 0 || num_kv_heads <= 0 ||
+      num_q_heads % num_kv_heads || max_blocks_per_seq <= 0 || num_blocks <= 0 ||
+      max_context_len < 0 || max_query_len < 0)
+    return PA_ERR_SHAPE;
+  if (num_seqs == 0 || num_query_tokens == 0 || max_query_len == 0) return PA_OK;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start)
+    return PA_ERR_NULL;
+  // Query rows per KV head; past one 16-row tile, items take two tiles so
+  // that each K/V tile load serves 32 rows.
+  const int64_t rows = std::min<int64_t>(max_query_len, num_query_tokens) *
+                       (num_q_heads / num_kv_heads);
+  const int row_tiles = rows > 16 ? 2 : 1;
+  const int64_t units = ceil_div(rows, 16 * row_tiles);
+  if (units * num_kv_heads > INT_MAX) return PA_ERR_SHAPE;
+
+  const int64_t max_len =
+      std::min<int64_t>(max_context_len, (int64_t)max_blocks_per_seq * block_size);
+  int64_t part_blocks, parts;
+  if (partition_size == 0) {
+    part_blocks = ceil_div(std::max<int64_t>(max_len, 1), kBlock);
+    parts = 1;
+  } else {
+    part_blocks = partition_size / kBlock;
+    parts = std::max<int64_t>(1, ceil_div(max_len, partition_size));
+  }
+  if (parts > kMaxGridYZ) return PA_ERR_SHAPE;
+  const WsLayout ws = ws_layout(num_query_tokens, num_q_heads, head_dim, parts);
+  const size_t need =
+      ws.total ? ws.total + align256((size_t)num_query_tokens * sizeof(int32_t)) : 0;
+  if (need && (!workspace || workspace_bytes < need)) return PA_ERR_WORKSPACE;
+
+  pa::MultiQueryArgs m{};
+  pa::DecodeArgs& a = m.d;
+  char* wsb = static_cast<char*>(workspace);
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.tmp_out = parts > 1 ? reinterpret_cast<float*>(wsb + ws.tmp_out) : nullptr;
+  a.max_logits = parts > 1 ? reinterpret_cast<float*>(wsb + ws.max_logits) : nullptr;
+  a.exp_sums = parts > 1 ? reinterpret_cast<float*>(wsb + ws.exp_sums) : nullptr;
+  a.num_seqs = num_seqs;
+  a.num_blocks_i32 = (int)std::min<int64_t>(num_blocks, INT32_MAX);
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.max_len = (int)max_len;
+  a.part_blocks = (int)part_blocks;
+  a.max_partitions = (int)parts;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.block_size = block_size;
+  m.query_start = query_start;
+  m.token_lens = parts > 1 ? reinterpret_cast<int32_t*>(wsb + ws.total) : nullptr;
+  m.num_query_tokens = num_query_tokens;
+  m.max_query_len = max_query_len;
+  m.row_tiles = row_tiles;
+  m.units = (int)units;
+
+  const hipStream_t st = (hipStream_t)stream;
+  if (pa::launch_multi_query(m, dtype, head_dim, st) != hipSuccess) return PA_ERR_LAUNCH;
+  if (parts > 1) {
+    // rows (query token, head) with the causal length of each token
+    pa::ReduceArgs r{};
+    r.out = out;
+    r.max_logits = a.max_logits;
+    r.exp_sums = a.exp_sums;
+    r.tmp_out = a.tmp_out;
+    r.context_lens = m.token_lens;
+    r.num_q_heads = num_q_heads;
+    r.partition_size = partition_size;
+    r.max_partitions = (int)parts;
+    r.max_len = (int)max_len;
+    r.skip_single = 1;
+    if (pa::launch_reduce(r, dtype, head_dim, num_query_tokens, st) != hipSuccess)
+      return PA_ERR_LAUNCH;
+  }
+  return PA_OK;
+}
+
+int pa_validate_query_start_host(const int32_t* query_start, const int32_t* context_lens,
+                                 int32_t num_seqs, int32_t num_query_tokens,
+                                 int32_t max_query_len) {
+  if (num_seqs < 0 || num_query_tokens < 0 || max_query_len < 0) return PA_ERR_SHAPE;
+  if (!query_start) return PA_ERR_NULL;
+  if (query_start[0] != 0 || query_start[num_seqs] != num_query_tokens) return PA_ERR_RANGE;
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    const int64_t n = (int64_t)query_start[s + 1] - query_start[s];
+    if (n < 0 || n > max_query_len) return PA_ERR_RANGE;
+    if (context_lens && n > context_lens[s]) return PA_ERR_RANGE;
+  }
+  return PA_OK;
+}
+
 int pa_paged_attention_reduce(void* out, const float* max_logits, const float* exp_sums,
                               const float* tmp_out, const int32_t* context_lens, int32_t num_seqs,
                               int32_t num_q_heads, int32_t head_dim, int32_t partition_size,

@@ -45,6 +45,20 @@ struct PrefixOut {
   float* o;
 };
 
+// Multi-token queries (query tokens t of sequence s: query_start[s] <=
+// t < query_start[s + 1]).  `d.q` and `d.out` are [T, Hq, D]; the partials
+// are laid out as in decode with one row per (query token, query head).
+struct MultiQueryArgs {
+  DecodeArgs d;
+  const int32_t* query_start;  // [B + 1]
+  int32_t* token_lens;         // [T] causal length of each query token, written for the
+                               // reduce (nullptr: a single partition)
+  int num_query_tokens;        // T
+  int max_query_len;           // query tokens per sequence are clamped to this
+  int row_tiles;               // 16-row tiles per item: 1 or 2
+  int units;                   // items per KV head: ceil(max_query_len * G / (16 * row_tiles))
+};
+
 struct ReduceArgs {
   void* out;
   const float* max_logits;
@@ -80,6 +94,11 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, int dtype, int head_dim, hipS
 // run (f16/bf16, at most 8 query heads per KV head).
 hipError_t launch_prefix(const DecodeArgs& a, const PrefixOut& o, int dtype, int head_dim,
                          hipStream_t stream);
+
+// Matrix-core multi-query attention: one workgroup per (kv head x 16-row
+// unit, sequence, partition) item (f16/bf16).
+hipError_t launch_multi_query(const MultiQueryArgs& a, int dtype, int head_dim,
+                              hipStream_t stream);
 
 hipError_t launch_reduce(const ReduceArgs& a, int dtype, int head_dim, int num_seqs,
                          hipStream_t stream);

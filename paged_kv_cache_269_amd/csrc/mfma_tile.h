@@ -193,15 +193,18 @@ __device__ __forceinline__ void stage_k(u32x4* kst, u32x4 (&kr)[D / 32], const M
   for (int jj = 0; jj < NJ; ++jj) kr[jj] = kst[kslot<D>(ln.tok_k, 4 * jj + ln.g)];
 }
 
-// Fold one tile (`limit` of its 16 tokens in the context) into the state.
+// Fold one tile (`limit` of its 16 tokens in the context) into the state;
+// K already in the S operand layout (stage_k), so several row tiles can
+// share one staged tile.  `row_limit` (per lane: its query row n) may stop a
+// row's tokens earlier (causal rows of a multi-token query); tokens past
+// `limit` are removed from V as well, for every row.
 template <int DT, int D, bool MASKED>
-__device__ __forceinline__ void consume_tile(MfmaState<D>& st, const u32x4 (&qb)[D / 32],
-                                             u32x4 (&kr)[D / 32],
-                                             typename MfmaShape<DT, D>::VT (&vr)[4], int limit,
-                                             float scale_log2, const MfmaLane& ln, u32x4* kst) {
+__device__ __forceinline__ void fold_tile(MfmaState<D>& st, const u32x4 (&qb)[D / 32],
+                                          const u32x4 (&kr)[D / 32],
+                                          typename MfmaShape<DT, D>::VT (&vr)[4], int limit,
+                                          int row_limit, float scale_log2, const MfmaLane& ln) {
   using S = MfmaShape<DT, D>;
   using VT = typename S::VT;
-  stage_k<D>(kst, kr, ln);
   f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int jj = 0; jj < S::NJ; ++jj) sacc = mfma_qk<DT>(kr[jj], qb[jj], sacc);
@@ -210,9 +213,8 @@ __device__ __forceinline__ void consume_tile(MfmaState<D>& st, const u32x4 (&qb)
   for (int e = 0; e < 4; ++e) {
     sc[e] = sacc[e] * scale_log2;
     if constexpr (MASKED) {
-      const bool ok = ln.g + 4 * e < limit;
-      sc[e] = ok ? sc[e] : -INFINITY;
-      if (!ok) vr[e] = VT{};  // whatever the slot holds must not reach P.V
+      sc[e] = ln.g + 4 * e < row_limit ? sc[e] : -INFINITY;
+      if (ln.g + 4 * e >= limit) vr[e] = VT{};  // whatever the slot holds must not reach P.V
     }
   }
   float mb = __builtin_fmaxf(__builtin_fmaxf(sc[0], sc[1]), __builtin_fmaxf(sc[2], sc[3]));
@@ -256,15 +258,26 @@ __device__ __forceinline__ void consume_tile(MfmaState<D>& st, const u32x4 (&qb)
   }
 }
 
+// Stage the tile's K, then fold it in.
+template <int DT, int D, bool MASKED>
+__device__ __forceinline__ void consume_tile(MfmaState<D>& st, const u32x4 (&qb)[D / 32],
+                                             u32x4 (&kr)[D / 32],
+                                             typename MfmaShape<DT, D>::VT (&vr)[4], int limit,
+                                             int row_limit, float scale_log2, const MfmaLane& ln,
+                                             u32x4* kst) {
+  stage_k<D>(kst, kr, ln);
+  fold_tile<DT, D, MASKED>(st, qb, kr, vr, limit, row_limit, scale_log2, ln);
+}
+
 template <int DT, int D>
 __device__ __forceinline__ void consume_any(MfmaState<D>& st, const u32x4 (&qb)[D / 32],
                                             u32x4 (&kr)[D / 32],
                                             typename MfmaShape<DT, D>::VT (&vr)[4], int limit,
                                             float scale_log2, const MfmaLane& ln, u32x4* kst) {
   if (limit == kBlockSize)
-    consume_tile<DT, D, false>(st, qb, kr, vr, limit, scale_log2, ln, kst);
+    consume_tile<DT, D, false>(st, qb, kr, vr, limit, limit, scale_log2, ln, kst);
   else
-    consume_tile<DT, D, true>(st, qb, kr, vr, limit, scale_log2, ln, kst);
+    consume_tile<DT, D, true>(st, qb, kr, vr, limit, limit, scale_log2, ln, kst);
 }
 
 }  // namespace pa

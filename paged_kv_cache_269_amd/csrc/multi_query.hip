@@ -1,0 +1,267 @@
+// Paged attention for several new query tokens per sequence (chunked
+// prefill, verification of drafted tokens) on the gfx950 matrix cores.
+//
+// Query token i of a sequence with n new tokens and a context of L tokens
+// (the new ones included, their K/V already in the cache) sits at position
+// p = L - n + i and attends to tokens 0 .. p: the decode definition
+// o_t = Attention(q_t, K_{1:t}, V_{1:t}) of "vLLM 2026 推理引擎全解"
+// (chenxutan.com) §1.1, for several t in one pass (same page, §4.1: the
+// target model checks all drafted tokens in one forward pass; vLLM manual
+// (doramagic.ai), FlashAttention backend: variable-length attention with
+// per-sequence query and key offsets).
+//
+// Rows of the matrix-core tile (mfma_tile.h) are (query token, query head)
+// pairs of one KV head, token-major: row R of (sequence, KV head) is token
+// R / G, head kvh * G + R % G.  A 16-row unit streams the K/V tiles up to
+// the position of its last row once; rows whose position ends inside a tile
+// mask the rest of it, and a tile that every row of the unit sees whole goes
+// down the unmasked path.  The NW waves of a workgroup take every NW-th tile
+// and merge through LDS; rows with several partitions leave partials for the
+// log-sum-exp reduce, with each query token's causal length beside them.
+#include <type_traits>
+
+#include "common.h"
+#include "items.h"
+#include "launch.h"
+#include "mfma_tile.h"
+
+namespace pa {
+
+namespace {
+
+// Workgroup shape: waves and tiles in flight per wave.
+constexpr int kMqWaves = 4;
+constexpr int kMqDepth = 2;
+
+// Grid: x = KV head + Hkv * unit (the units of one KV head of a sequence read
+// the same tiles; with Hkv a multiple of the 8 XCDs they land on one XCD and
+// share its L2), y = sequence slot (longest context first), z = partition.
+// An item holds RT 16-row tiles: every staged K/V tile is folded into each.
+template <int DT, int D, int NW, int DEPTH, int BS, int RT>
+__global__ __launch_bounds__(NW * 64) void multi_query_kernel(MultiQueryArgs ma) {
+  using S = MfmaShape<DT, D>;
+  using VT = typename S::VT;
+  constexpr int EPL = S::EPL;
+  __shared__ MfmaLds<D, NW> sm;
+  __shared__ u32x4 kst_all[NW][kKStageSlots<D>];
+  const DecodeArgs& a = ma.d;
+  const int G = a.num_q_heads / a.num_kv_heads;
+  const int kvh = blockIdx.x % a.num_kv_heads, unit = blockIdx.x / a.num_kv_heads;
+  const int s = longest_first(a, blockIdx.y), part = blockIdx.z;
+  const int L = clamp_len(a, s);
+
+  // Query tokens of s, kept inside [0, T) and to max_query_len.
+  const int T = ma.num_query_tokens;
+  const int t0 = ma.query_start[s];
+  int nq = ma.query_start[s + 1] - t0;
+  nq = (t0 < 0 || t0 > T) ? 0 : max(0, min(nq, min(ma.max_query_len, T - t0)));
+  const int base_pos = L - nq;  // position of query token 0
+  if (ma.token_lens != nullptr && kvh == 0 && unit == 0 && part == 0)
+    for (int i = threadIdx.x; i < nq; i += NW * 64) ma.token_lens[t0 + i] = max(base_pos + i + 1, 0);
+
+  const int r0 = unit * 16 * RT;
+  if (r0 >= nq * G) return;  // past this sequence's rows
+  const int rows = min(16 * RT, nq * G - r0);
+  const int span = max(base_pos + (r0 + rows - 1) / G + 1, 0);  // tokens the item reads
+  const int nblocks = (span + kBlockSize - 1) / kBlockSize;
+  if (part >= parts_of(span, a.part_blocks)) return;
+
+  const MfmaLane ln;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  u32x4* kst = kst_all[w];
+  // Row tile r: rows r0 + 16 r + n.  Per lane (row n of each tile) the
+  // position of its query token (idle rows take the tile's last row's, so
+  // they never narrow the unmasked test) and its q slices.
+  int rows_t[RT], pos_first[RT], pos_n[RT];
+  u32x4 qb[RT][S::NJ];
+  const u32x4* q = reinterpret_cast<const u32x4*>(a.q);
+  static_for<0, RT>([&](auto rc) __attribute__((always_inline)) {
+    constexpr int r = decltype(rc)::value;
+    const int rb = r0 + 16 * r;
+    rows_t[r] = max(0, min(16, rows - 16 * r));
+    pos_first[r] = base_pos + rb / G;
+    const bool active = ln.n < rows_t[r];
+    const int rn = rb + (active ? ln.n : max(rows_t[r] - 1, 0));
+    pos_n[r] = base_pos + rn / G;
+    const int64_t qrow = (int64_t)(t0 + rn / G) * a.num_q_heads + kvh * G + rn % G;
+#pragma unroll
+    for (int jj = 0; jj < S::NJ; ++jj)
+      qb[r][jj] = active ? q[qrow * S::CPR + 4 * jj + ln.g] : u32x4{0u, 0u, 0u, 0u};
+  });
+
+  const int32_t* __restrict__ bt = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
+  const int jb = part * a.part_blocks;
+  const int je = min(jb + a.part_blocks, nblocks);
+  const int j0 = jb + w;                                   // tiles j0, j0 + NW, ...
+  const int nk = je > j0 ? (je - j0 + NW - 1) / NW : 0;   // how many
+
+  MfmaState<D> st[RT];
+  static_for<0, RT>([&](auto rc) __attribute__((always_inline)) { st[decltype(rc)::value].reset(); });
+
+  auto id_at = [&](int kk) __attribute__((always_inline)) {
+    return tile_ids<BS>(bt, j0 + min(kk, nk - 1) * NW, a.max_blocks_per_seq);
+  };
+  // Descriptors of the wave's kk-th tile, its index and its token count
+  // (tokens up to the item's last position, inside the pool).
+  auto tile = [&](int kk, const TileIds<BS>& ids, int& limit, int& jt) __attribute__((always_inline)) {
+    jt = j0 + min(kk, nk - 1) * NW;
+    const bool ok = kk < nk;
+    limit = ok ? tile_limit<BS>(a, ids, span - jt * kBlockSize) : 0;
+    return tile_desc<BS, S::TILE_BYTES>(a, ids, jt, kvh, ok);
+  };
+  // (The lambdas here are forced inline: a call would leave everything they
+  // capture in scratch memory.)
+  // Stage tile jt's K once, fold it into every live row tile; rows stop at
+  // their own position.  The tests are wave-uniform: every row of a tile
+  // sees the whole K/V tile when its first row does.
+  auto consume = [&](u32x4 (&kr)[S::NJ], VT (&vr)[4], int limit,
+                     int jt) __attribute__((always_inline)) {
+    stage_k<D>(kst, kr, ln);
+    static_for<0, RT>([&](auto rc) __attribute__((always_inline)) {
+      constexpr int r = decltype(rc)::value;
+      if (r > 0 && rows_t[r] == 0) return;
+      if (limit == kBlockSize && pos_first[r] + 1 >= (jt + 1) * kBlockSize) {
+        fold_tile<DT, D, false>(st[r], qb[r], kr, vr, limit, limit, a.scale_log2, ln);
+      } else {
+        const int rl = min(limit, max(0, pos_n[r] + 1 - jt * kBlockSize));
+        fold_tile<DT, D, true>(st[r], qb[r], kr, vr, limit, rl, a.scale_log2, ln);
+      }
+    });
+  };
+
+  // Software pipeline as in decode: DEPTH register sets, loads issued on
+  // every step (empty past the end) so the wait counts never branch.
+  u32x4 kr[DEPTH][S::NJ];
+  VT vr[DEPTH][4];
+  int lim[DEPTH], jts[DEPTH];
+  auto pipeline = [&](auto shared) __attribute__((always_inline)) {
+    constexpr bool SH = decltype(shared)::value;
+    static_for<0, DEPTH - 1>([&](auto dc) __attribute__((always_inline)) {
+      constexpr int d = decltype(dc)::value;
+      load_tile<DT, D, SH>(tile(d, id_at(d), lim[d], jts[d]), ln, kr[d], vr[d]);
+    });
+    TileIds<BS> next_id = id_at(DEPTH - 1);
+    for (int k = 0; k < nk; k += DEPTH) {
+      static_for<0, DEPTH>([&](auto dc) __attribute__((always_inline)) {
+        constexpr int d = decltype(dc)::value;
+        constexpr int dn = (d + DEPTH - 1) % DEPTH;
+        const int kn = k + d + DEPTH - 1;
+        const TileIds<BS> id = next_id;
+        next_id = id_at(kn + 1);
+        load_tile<DT, D, SH>(tile(kn, id, lim[dn], jts[dn]), ln, kr[dn], vr[dn]);
+        consume(kr[d], vr[d], lim[d], jts[d]);
+      });
+    }
+  };
+  if (nk > 0) {
+    // Tiles read again soon -- by the other units of this KV head, or by the
+    // neighbouring sequence when it maps the same first block -- load with
+    // the cache-allocating policy; the rest stream past the caches.
+    const int32_t* nb = a.num_seqs > 1 ? a.block_tables +
+                            (int64_t)(s > 0 ? s - 1 : s + 1) * a.max_blocks_per_seq : nullptr;
+    const bool reread = nq * G > 16 * RT ||
+                        (nb != nullptr && tile_ids<BS>(nb, j0, a.max_blocks_per_seq).id[0] ==
+                                              tile_ids<BS>(bt, j0, a.max_blocks_per_seq).id[0]);
+    if (reread)
+      pipeline(std::true_type{});
+    else
+      pipeline(std::false_type{});
+  }
+
+  // Per row tile: this wave's per-row totals, then the cross-wave merge
+  // through LDS (one tile at a time, reusing the same LDS).
+  const int n = ln.n, g = ln.g;
+  static_for<0, RT>([&](auto rc) __attribute__((always_inline)) {
+    constexpr int r = decltype(rc)::value;
+    if (rows_t[r] == 0) return;  // uniform over the workgroup
+    if (r > 0) __syncthreads();  // the previous tile's readers are done
+    float lsum = xor16_combine(st[r].lsum, AddOp{});
+    lsum = xor32_combine(lsum, AddOp{});
+    if (g == 0) {
+      sm.m[w][n] = st[r].m;
+      sm.l[w][n] = lsum;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+      for (int jj = 0; jj < EPL; ++jj) sm.o[w][4 * g + e][EPL * n + jj] = st[r].o[jj][e];
+    __syncthreads();
+    if (threadIdx.x < 16) {
+      const int hh = threadIdx.x;
+      float M = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < NW; ++i) M = __builtin_fmaxf(M, sm.m[i][hh]);
+      float tot = 0.f;
+      float f[NW];
+#pragma unroll
+      for (int i = 0; i < NW; ++i) {
+        f[i] = (sm.m[i][hh] == -INFINITY) ? 0.f : fast_exp2(sm.m[i][hh] - M);
+        tot += sm.l[i][hh] * f[i];
+      }
+      const float inv = tot > 0.f ? 1.f / tot : 0.f;
+#pragma unroll
+      for (int i = 0; i < NW; ++i) sm.f[i][hh] = f[i] * inv;
+      sm.tot[hh] = tot;
+      sm.mx[hh] = M;
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < rows_t[r] * D; i += NW * 64) {
+      const int hh = i / D, d = i % D;
+      const int R = r0 + 16 * r + hh, tok = R / G;
+      // partitions of this row's own causal span; later ones are not its
+      const int row_parts = parts_of(max(base_pos + tok + 1, 0), a.part_blocks);
+      if (part >= row_parts) continue;
+      float v = 0.f;
+#pragma unroll
+      for (int k = 0; k < NW; ++k) v += sm.o[k][hh][d] * sm.f[k][hh];
+      const int64_t orow = (int64_t)(t0 + tok) * a.num_q_heads + kvh * G + R % G;
+      if (row_parts <= 1) {
+        store_elem<DT>(a.out, orow * D + d, v);
+      } else {
+        const int64_t prow = orow * a.max_partitions + part;
+        a.tmp_out[prow * D + d] = v;
+        if (d == 0) {
+          a.max_logits[prow] = sm.mx[hh] * kLn2;
+          a.exp_sums[prow] = sm.tot[hh];
+        }
+      }
+    }
+  });
+}
+
+template <int DT, int D, int BS>
+hipError_t launch_bs(const MultiQueryArgs& a, hipStream_t stream) {
+  const dim3 grid((unsigned)(a.d.num_kv_heads * a.units), (unsigned)a.d.num_seqs,
+                  (unsigned)a.d.max_partitions);
+  if (a.row_tiles == 2)
+    hipLaunchKernelGGL((multi_query_kernel<DT, D, kMqWaves, kMqDepth, BS, 2>), grid,
+                       dim3(kMqWaves * 64), 0, stream, a);
+  else
+    hipLaunchKernelGGL((multi_query_kernel<DT, D, kMqWaves, kMqDepth, BS, 1>), grid,
+                       dim3(kMqWaves * 64), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <int DT, int D>
+hipError_t launch_typed(const MultiQueryArgs& a, hipStream_t stream) {
+  switch (a.d.block_size) {
+    case 8: return launch_bs<DT, D, 8>(a, stream);
+    case 32: return launch_bs<DT, D, 32>(a, stream);
+    default: return launch_bs<DT, D, 16>(a, stream);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_multi_query(const MultiQueryArgs& a, int dtype, int head_dim,
+                              hipStream_t stream) {
+  switch (dtype * 1000 + head_dim) {
+    case kF16 * 1000 + 64: return launch_typed<kF16, 64>(a, stream);
+    case kF16 * 1000 + 128: return launch_typed<kF16, 128>(a, stream);
+    case kBF16 * 1000 + 64: return launch_typed<kBF16, 64>(a, stream);
+    case kBF16 * 1000 + 128: return launch_typed<kBF16, 128>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace pa

@@ -22,6 +22,9 @@ new-token V):
   workload uses a fixed 32-page pool.
 * Values: float32 N(0,1) rounded to nearest-even into the element type.
   bfloat16 arrays are held as uint16 bit patterns.
+* Multi-token queries (generate_query_spans): q rows for the last n_s tokens
+  of each context, N(0,1) from their own seed; the cache already holds those
+  tokens' K/V.
 * Poison (parity runs): every slot no sequence owns -- the tail of a last
   page, pages nobody uses and the slot the new token is about to fill -- is
   NaN, so a read of it shows up in the output.
@@ -263,6 +266,51 @@ def generate(name: str, poison: bool = True, threads: Optional[int] = None,
                     shared_prefix_blocks=shared, context_lens=lens.astype(np.int32),
                     block_tables=tables, slot_mapping=slots, q=q, key=key, value=value,
                     k_cache=k_cache, v_cache=v_cache, params=p)
+
+
+# ---------------------------------------------------------------------------
+# several new query tokens per sequence (chunked prefill, drafted tokens)
+
+@dataclasses.dataclass
+class QuerySpans:
+    q: np.ndarray            # [T, Hq, D] query rows, token-major
+    query_start: np.ndarray  # [B + 1] int32
+    query_lens: np.ndarray   # [B] int32
+    max_query_len: int
+
+    @property
+    def num_tokens(self) -> int:
+        return int(self.query_start[-1])
+
+
+def generate_query_spans(w: Workload, query_lens, seed: int = 0) -> QuerySpans:
+    """Query rows for the last n_s tokens of every context of ``w`` (their K/V
+    are the pool's own, in place once the workload's KV write has run).
+    ``query_lens``: one int for every sequence (capped at its length) or one
+    per sequence, taken as given; q ~ N(0, 1) rounded into the workload's
+    element type, drawn from SeedSequence(seed)."""
+    B = w.num_seqs
+    if np.ndim(query_lens) == 0:
+        n = np.minimum(int(query_lens), w.context_lens).astype(np.int64)
+    else:
+        n = np.asarray(query_lens, np.int64)
+        if n.shape != (B,) or (n < 0).any():
+            raise ValueError("one non-negative query length per sequence")
+    qs = np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
+    q = _normal(np.random.SeedSequence(seed), (int(qs[-1]), w.num_q_heads, w.head_dim), w.dtype)
+    return QuerySpans(q=q, query_start=qs, query_lens=n.astype(np.int32),
+                      max_query_len=max(1, int(n.max(initial=0))))
+
+
+def multi_query_flops(w: Workload, spans: QuerySpans) -> int:
+    """Score and output products of a multi-query pass: query token i of a
+    span sees p + 1 = L - n + i + 1 tokens; per query head and seen token a
+    D-long dot product and a D-long multiply-add, 2 flops each."""
+    seen = 0
+    for L, n in zip(w.context_lens.astype(np.int64), spans.query_lens.astype(np.int64)):
+        p1 = np.maximum(L - n + np.arange(n) + 1, 0)
+        seen += int(p1.sum())
+    return 4 * seen * w.num_q_heads * w.head_dim
 
 
 # ---------------------------------------------------------------------------

@@ -114,6 +114,53 @@ def test_cascade_argument_checks_and_workspace(hiplib):
     assert _cascade(lib, B=0, out=None, ws=None, wsb=0) == OK
 
 
+def _mq(lib, **kw):
+    a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, cl=FAKE, qs=FAKE, B=2, T=8, Hq=8, Hkv=2,
+             D=128, bs=16, M=4, N=10, scale=0.1, dtype=1, mq=4, part=512, maxlen=64, ws=None,
+             wsb=0, stream=None)
+    a.update(kw)
+    return lib.pa_paged_attention_multi_query(
+        a["out"], a["q"], a["k"], a["v"], a["bt"], a["cl"], a["qs"], a["B"], a["T"], a["Hq"],
+        a["Hkv"], a["D"], a["bs"], a["M"], a["N"], a["scale"], a["dtype"], a["mq"], a["part"],
+        a["maxlen"], a["ws"], a["wsb"], a["stream"])
+
+
+def test_multi_query_argument_checks_and_workspace(hiplib):
+    lib = hiplib.load_library()
+    assert _mq(lib, qs=None) == NULL
+    assert _mq(lib, out=None) == NULL
+    assert _mq(lib, dtype=0) == UNSUP          # float32 is not taken here
+    assert _mq(lib, D=96) == UNSUP
+    assert _mq(lib, bs=24) == UNSUP
+    assert _mq(lib, part=100) == UNSUP
+    assert _mq(lib, Hq=6, Hkv=4) == SHAPE
+    assert _mq(lib, T=70000) == SHAPE
+    assert _mq(lib, B=-1) == SHAPE
+    assert _mq(lib, mq=-1) == SHAPE
+    assert _mq(lib, maxlen=1024, M=64) == WS   # partials for 2 partitions
+    f = lib.pa_multi_query_workspace_bytes
+    need = f(8, 8, 128, 1024, 512)
+    al = lambda x: -(-x // 256) * 256
+    rows = 8 * 8 * 2
+    assert need == al(rows * 128 * 4) + 2 * al(rows * 4) + al(8 * 4)
+    assert _mq(lib, maxlen=1024, M=64, ws=FAKE, wsb=need - 1) == WS
+    assert f(8, 8, 128, 512, 512) == 0 and f(8, 8, 128, 4096, 0) == 0 and f(-1, 8, 128, 9, 16) == 0
+    # nothing to do: no pointer is looked at
+    assert _mq(lib, T=0, out=None) == OK and _mq(lib, B=0, qs=None) == OK
+
+
+def test_query_start_validator(hiplib):
+    v = hiplib.validate_query_start_host
+    assert v([0, 3, 3, 7], [5, 1, 9], 7, 4) == 0
+    assert v([0, 3, 3, 7], None, 7, 4) == 0
+    assert v([1, 3, 3, 7], None, 7, 4) == RANGE       # must start at 0
+    assert v([0, 3, 3, 6], None, 7, 4) == RANGE       # must end at T
+    assert v([0, 3, 2, 7], None, 7, 5) == RANGE       # decreasing
+    assert v([0, 3, 3, 7], None, 7, 3) == RANGE       # a span longer than max_query_len
+    assert v([0, 3, 3, 7], [2, 1, 9], 7, 4) == RANGE  # more new tokens than context
+    assert v([0], None, 0, 1) == 0
+
+
 def test_reshape_and_reduce_argument_checks(hiplib):
     lib = hiplib.load_library()
     r = lib.pa_reshape_and_cache

@@ -436,3 +436,103 @@ def test_generator_is_deterministic_and_poisoned():
     # the new token's slot is poisoned before the write
     s0 = a.slot_mapping[0]
     assert np.all(a.k_cache[s0 // 16, :, s0 % 16] == 0x7FC0)
+
+
+# ---------------------------------------------------------------------------
+# P12: several new query tokens per sequence (§1.1's o_t for each new t)
+
+def mq_case(rng, lens, nqs, Hq, Hkv, D, dtype):
+    """Dense K/V per sequence, paged under a random permutation, and q rows
+    for the last n_s tokens of each context."""
+    _, Kd, Vd, N = make_dense_case(rng, lens, Hq, Hkv, D, dtype)
+    kc, vc, tables = scatter_to_pool(Kd, Vd, lens, N, rng, dtype, Hkv, D)
+    T = int(sum(nqs))
+    q = from_f32(rng.standard_normal((T, Hq, D)), dtype)
+    qs = np.concatenate([[0], np.cumsum(nqs)]).astype(np.int32)
+    return q, Kd, Vd, kc, vc, tables, qs
+
+
+def dense_kv(Kd, Vd, s, dtype, G):
+    K = torch.from_numpy(to_f64(Kd[s], dtype)).permute(1, 0, 2).repeat_interleave(G, 0)
+    V = torch.from_numpy(to_f64(Vd[s], dtype)).permute(1, 0, 2).repeat_interleave(G, 0)
+    return K, V                                                   # [Hq, L, D]
+
+
+@pytest.mark.parametrize("dtype,G", [("f32", 1), ("bf16", 4)])
+def test_multi_query_whole_prompt_equals_causal_sdpa(dtype, G):
+    """Every token of a prompt as a query (n = L): torch's causal attention
+    (square lower-triangular mask) on the dense K/V."""
+    rng = np.random.default_rng(21)
+    lens = [37, 16, 1]
+    Hkv, D = 2, 64
+    Hq = Hkv * G
+    q, Kd, Vd, kc, vc, tables, qs = mq_case(rng, lens, lens, Hq, Hkv, D, dtype)
+    scale = 1 / math.sqrt(D)
+    out = oracle.multi_query(q, kc, vc, tables, np.array(lens, np.int32), qs, scale, dtype)
+    for s, L in enumerate(lens):
+        K, V = dense_kv(Kd, Vd, s, dtype, G)
+        qq = torch.from_numpy(to_f64(q[qs[s]:qs[s + 1]], dtype)).permute(1, 0, 2)   # [Hq, L, D]
+        ref = torch.nn.functional.scaled_dot_product_attention(qq, K, V, is_causal=True,
+                                                               scale=scale)
+        np.testing.assert_allclose(out[qs[s]:qs[s + 1]], ref.permute(1, 0, 2).numpy(),
+                                   rtol=0, atol=1e-12)
+
+
+def test_multi_query_span_sits_at_the_end_of_the_context():
+    """n < L: token i of the span sees exactly tokens 0 .. L - n + i --
+    attention of that one query over that many leading dense rows (torch,
+    no mask); the last token of each span is plain decode over the whole
+    context."""
+    rng = np.random.default_rng(22)
+    lens, nqs = [50, 33, 17, 5], [4, 1, 16, 5]
+    Hkv, G, D, dtype = 2, 2, 64, "f16"
+    Hq = Hkv * G
+    q, Kd, Vd, kc, vc, tables, qs = mq_case(rng, lens, nqs, Hq, Hkv, D, dtype)
+    scale = 1 / math.sqrt(D)
+    cl = np.array(lens, np.int32)
+    out = oracle.multi_query(q, kc, vc, tables, cl, qs, scale, dtype)
+    for s, (L, n) in enumerate(zip(lens, nqs)):
+        K, V = dense_kv(Kd, Vd, s, dtype, G)
+        for i in range(n):
+            p = L - n + i
+            qq = torch.from_numpy(to_f64(q[qs[s] + i], dtype))[:, None, :]       # [Hq, 1, D]
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                qq, K[:, :p + 1], V[:, :p + 1], scale=scale)
+            np.testing.assert_allclose(out[qs[s] + i], ref[:, 0].numpy(), rtol=0, atol=1e-12)
+    last = qs[1:] - 1
+    dec = oracle.decode(q[last], kc, vc, tables, cl, scale, dtype)
+    np.testing.assert_array_equal(out[last], dec)
+
+
+def test_multi_query_causal_boundary():
+    """Changing K/V of token p + 1 leaves query row p unchanged; changing
+    token p changes it (an off-by-one in the mask fails one of the two)."""
+    rng = np.random.default_rng(23)
+    L, n, Hkv, D, dtype = 40, 6, 1, 64, "f32"
+    q, Kd, Vd, kc, vc, tables, qs = mq_case(rng, [L], [n], 1, Hkv, D, dtype)
+    cl = np.array([L], np.int32)
+    base = oracle.multi_query(q, kc, vc, tables, cl, qs, 0.125, dtype)
+    for i in range(n - 1):
+        p = L - n + i
+        for tok, should_change in ((p + 1, False), (p, True)):
+            k2, v2 = kc.copy(), vc.copy()
+            b = tables[0, tok // BS]
+            k2[b, 0, tok % BS] += 1.0
+            v2[b, 0, tok % BS] += 1.0
+            got = oracle.multi_query(q, k2, v2, tables, cl, qs, 0.125, dtype)
+            changed = not np.array_equal(got[i], base[i])
+            assert changed == should_change, (i, tok)
+
+
+def test_multi_query_span_longer_than_context_gives_zero_rows():
+    """Tokens whose position would fall before the context start (n > L)
+    attend to nothing: zero rows; the rest are unaffected."""
+    rng = np.random.default_rng(24)
+    q, Kd, Vd, kc, vc, tables, qs = mq_case(rng, [3], [3], 2, 2, 64, "f32")
+    cl = np.array([3], np.int32)
+    q5 = from_f32(rng.standard_normal((5, 2, 64)), "f32")
+    q5[2:] = q
+    out = oracle.multi_query(q5, kc, vc, tables, cl, np.array([0, 5], np.int32), 0.125, "f32")
+    assert (out[:2] == 0).all()
+    ref = oracle.multi_query(q, kc, vc, tables, cl, qs, 0.125, "f32")
+    np.testing.assert_array_equal(out[2:], ref)
