@@ -291,12 +291,15 @@ int pa_paged_attention_multi_query(void* out, const void* q, const void* k_cache
   if (num_seqs == 0 || num_query_tokens == 0 || max_query_len == 0) return PA_OK;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start)
     return PA_ERR_NULL;
-  // Query rows per KV head; past one 16-row tile, items take two tiles so
-  // that each K/V tile load serves 32 rows.
+  // Query rows per KV head.  Up to 64: items of one or two 16-row tiles
+  // whose waves split the K/V tiles; more: wide items of 4 waves owning 32
+  // rows each, which share every K/V tile through LDS.
   const int64_t rows = std::min<int64_t>(max_query_len, num_query_tokens) *
                        (num_q_heads / num_kv_heads);
-  const int row_tiles = rows > 16 ? 2 : 1;
-  const int64_t units = ceil_div(rows, 16 * row_tiles);
+  const int wide = rows > 64 ? 1 : 0;
+  const int row_tiles = wide ? 2 : (rows > 16 ? 2 : 1);
+  const int64_t item_rows = wide ? 4 * 16 * row_tiles : 16 * row_tiles;
+  const int64_t units = ceil_div(rows, item_rows);
   if (units * num_kv_heads > INT_MAX) return PA_ERR_SHAPE;
 
   const int64_t max_len =
@@ -341,8 +344,10 @@ int pa_paged_attention_multi_query(void* out, const void* q, const void* k_cache
   m.token_lens = parts > 1 ? reinterpret_cast<int32_t*>(wsb + ws.total) : nullptr;
   m.num_query_tokens = num_query_tokens;
   m.max_query_len = max_query_len;
+  m.wide = wide;
   m.row_tiles = row_tiles;
   m.units = (int)units;
+  m.reread = units > 1 ? 1 : 0;
 
   const hipStream_t st = (hipStream_t)stream;
   if (pa::launch_multi_query(m, dtype, head_dim, st) != hipSuccess) return PA_ERR_LAUNCH;

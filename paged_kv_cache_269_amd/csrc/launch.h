@@ -55,8 +55,11 @@ struct MultiQueryArgs {
                                // reduce (nullptr: a single partition)
   int num_query_tokens;        // T
   int max_query_len;           // query tokens per sequence are clamped to this
-  int row_tiles;               // 16-row tiles per item: 1 or 2
-  int units;                   // items per KV head: ceil(max_query_len * G / (16 * row_tiles))
+  int wide;                    // 1: the waves of an item own disjoint row tiles and share
+                               //    every K/V tile through LDS; 0: they split the tiles
+  int row_tiles;               // 16-row tiles per item (1 or 2); wide items: 2 per wave
+  int units;                   // items per KV head
+  int reread;                  // 1: K/V tiles are read by several items (cache them)
 };
 
 struct ReduceArgs {

@@ -176,12 +176,11 @@ __device__ __forceinline__ int kslot(int r, int c) {
 template <int D>
 constexpr int kKStageSlots = kBlockSize * (D / 8 + 1);
 
-// K tile (as loaded: load jj, lane l = chunk jj*64 + l of the tile) through
-// the wave's own LDS tile into the S operand layout, in place: lane (n, g) of
-// product jj gets chunk 4jj + g of token row tau(n).  Only this wave touches
-// `kst`, and its LDS accesses complete in order, so no barrier is needed.
+// K tile as loaded (load jj, lane l = chunk jj*64 + l of the tile) into an
+// LDS staging tile, row-major with padded rows.
 template <int D>
-__device__ __forceinline__ void stage_k(u32x4* kst, u32x4 (&kr)[D / 32], const MfmaLane& ln) {
+__device__ __forceinline__ void put_k_stage(u32x4* kst, const u32x4 (&kr)[D / 32],
+                                            const MfmaLane& ln) {
   constexpr int CPR = D / 8, NJ = D / 32;
   const int lane = ln.n + 16 * ln.g;
 #pragma unroll
@@ -189,22 +188,56 @@ __device__ __forceinline__ void stage_k(u32x4* kst, u32x4 (&kr)[D / 32], const M
     const int idx = jj * 64 + lane;
     kst[kslot<D>(idx / CPR, idx % CPR)] = kr[jj];
   }
-#pragma unroll
-  for (int jj = 0; jj < NJ; ++jj) kr[jj] = kst[kslot<D>(ln.tok_k, 4 * jj + ln.g)];
 }
 
-// Fold one tile (`limit` of its 16 tokens in the context) into the state;
-// K already in the S operand layout (stage_k), so several row tiles can
-// share one staged tile.  `row_limit` (per lane: its query row n) may stop a
-// row's tokens earlier (causal rows of a multi-token query); tokens past
-// `limit` are removed from V as well, for every row.
+// The S operand layout out of a staging tile: lane (n, g) of product jj gets
+// chunk 4jj + g of token row tau(n).
+template <int D>
+__device__ __forceinline__ void get_k_stage(const u32x4* kst, u32x4 (&kr)[D / 32],
+                                            const MfmaLane& ln) {
+#pragma unroll
+  for (int jj = 0; jj < D / 32; ++jj) kr[jj] = kst[kslot<D>(ln.tok_k, 4 * jj + ln.g)];
+}
+
+// K tile through the wave's own LDS tile into the S operand layout, in
+// place.  Only this wave touches `kst`, and its LDS accesses complete in
+// order, so no barrier is needed.
+template <int D>
+__device__ __forceinline__ void stage_k(u32x4* kst, u32x4 (&kr)[D / 32], const MfmaLane& ln) {
+  put_k_stage<D>(kst, kr, ln);
+  get_k_stage<D>(kst, kr, ln);
+}
+
+// B operands of the tile's P.V products (product jj: this lane's tokens
+// g + 4e, element EPL*n + jj, packed in pairs), built once per tile; rows of
+// tokens past `limit` are zeroed first (whatever those slots hold must not
+// reach P.V, not even times a zero weight).
 template <int DT, int D, bool MASKED>
-__device__ __forceinline__ void fold_tile(MfmaState<D>& st, const u32x4 (&qb)[D / 32],
-                                          const u32x4 (&kr)[D / 32],
-                                          typename MfmaShape<DT, D>::VT (&vr)[4], int limit,
-                                          int row_limit, float scale_log2, const MfmaLane& ln) {
+__device__ __forceinline__ void v_operands(typename MfmaShape<DT, D>::VT (&vr)[4], int limit,
+                                           const MfmaLane& ln, u32x2 (&vb)[D / 16]) {
   using S = MfmaShape<DT, D>;
   using VT = typename S::VT;
+  if constexpr (MASKED) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (ln.g + 4 * e >= limit) vr[e] = VT{};
+  }
+#pragma unroll
+  for (int jj = 0; jj < S::EPL; ++jj)
+    vb[jj] = u32x2{S::VS::half(vr[0], jj) | (S::VS::half(vr[1], jj) << 16),
+                   S::VS::half(vr[2], jj) | (S::VS::half(vr[3], jj) << 16)};
+}
+
+// Fold one tile into the state: K already in the S operand layout
+// (stage_k), V as P.V operands (v_operands), so several row tiles can share
+// one tile.  Scores of tokens at or past `row_limit` (per lane: its query
+// row n; the tile's token count, or less for causal rows of a multi-token
+// query) are dropped.
+template <int DT, int D, bool MASKED>
+__device__ __forceinline__ void fold_tile(MfmaState<D>& st, const u32x4 (&qb)[D / 32],
+                                          const u32x4 (&kr)[D / 32], const u32x2 (&vb)[D / 16],
+                                          int row_limit, float scale_log2, const MfmaLane& ln) {
+  using S = MfmaShape<DT, D>;
   f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int jj = 0; jj < S::NJ; ++jj) sacc = mfma_qk<DT>(kr[jj], qb[jj], sacc);
@@ -212,10 +245,7 @@ __device__ __forceinline__ void fold_tile(MfmaState<D>& st, const u32x4 (&qb)[D 
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     sc[e] = sacc[e] * scale_log2;
-    if constexpr (MASKED) {
-      sc[e] = ln.g + 4 * e < row_limit ? sc[e] : -INFINITY;
-      if (ln.g + 4 * e >= limit) vr[e] = VT{};  // whatever the slot holds must not reach P.V
-    }
+    if constexpr (MASKED) sc[e] = ln.g + 4 * e < row_limit ? sc[e] : -INFINITY;
   }
   float mb = __builtin_fmaxf(__builtin_fmaxf(sc[0], sc[1]), __builtin_fmaxf(sc[2], sc[3]));
   mb = xor16_combine(mb, MaxOp{});
@@ -251,22 +281,20 @@ __device__ __forceinline__ void fold_tile(MfmaState<D>& st, const u32x4 (&qb)[D 
   st.lsum += (p[0] + p[1]) + (p[2] + p[3]);
   const u32x2 pa{pack2<DT>(p[0], p[1]), pack2<DT>(p[2], p[3])};
 #pragma unroll
-  for (int jj = 0; jj < S::EPL; ++jj) {
-    const u32x2 vb{S::VS::half(vr[0], jj) | (S::VS::half(vr[1], jj) << 16),
-                   S::VS::half(vr[2], jj) | (S::VS::half(vr[3], jj) << 16)};
-    st.o[jj] = mfma_pv<DT>(pa, vb, st.o[jj]);
-  }
+  for (int jj = 0; jj < S::EPL; ++jj) st.o[jj] = mfma_pv<DT>(pa, vb[jj], st.o[jj]);
 }
 
-// Stage the tile's K, then fold it in.
+// Fold one tile (`limit` of its 16 tokens in the context) into the state:
+// stage K, build the V operands, fold.
 template <int DT, int D, bool MASKED>
 __device__ __forceinline__ void consume_tile(MfmaState<D>& st, const u32x4 (&qb)[D / 32],
                                              u32x4 (&kr)[D / 32],
                                              typename MfmaShape<DT, D>::VT (&vr)[4], int limit,
-                                             int row_limit, float scale_log2, const MfmaLane& ln,
-                                             u32x4* kst) {
+                                             float scale_log2, const MfmaLane& ln, u32x4* kst) {
   stage_k<D>(kst, kr, ln);
-  fold_tile<DT, D, MASKED>(st, qb, kr, vr, limit, row_limit, scale_log2, ln);
+  u32x2 vb[D / 16];
+  v_operands<DT, D, MASKED>(vr, limit, ln, vb);
+  fold_tile<DT, D, MASKED>(st, qb, kr, vb, limit, scale_log2, ln);
 }
 
 template <int DT, int D>
@@ -275,9 +303,9 @@ __device__ __forceinline__ void consume_any(MfmaState<D>& st, const u32x4 (&qb)[
                                             typename MfmaShape<DT, D>::VT (&vr)[4], int limit,
                                             float scale_log2, const MfmaLane& ln, u32x4* kst) {
   if (limit == kBlockSize)
-    consume_tile<DT, D, false>(st, qb, kr, vr, limit, limit, scale_log2, ln, kst);
+    consume_tile<DT, D, false>(st, qb, kr, vr, limit, scale_log2, ln, kst);
   else
-    consume_tile<DT, D, true>(st, qb, kr, vr, limit, limit, scale_log2, ln, kst);
+    consume_tile<DT, D, true>(st, qb, kr, vr, limit, scale_log2, ln, kst);
 }
 
 }  // namespace pa

@@ -33,12 +33,43 @@ namespace {
 constexpr int kMqWaves = 4;
 constexpr int kMqDepth = 2;
 
+// Fold staged tile jt (`limit` tokens) into a wave's RT row tiles, one row
+// tile at a time (folding them side by side needs more registers than two
+// waves per SIMD leave).  Row tile r holds rows_t[r] rows whose query
+// positions run from pos_first[r] to pos_last[r] (pos_n[r]: this lane's
+// row); a row sees the tile's tokens up to its own position.  A row tile
+// none of whose rows sees the tile is skipped, one all of whose rows see
+// all of it goes unmasked.  All tests are wave-uniform.
+template <int DT, int D, int RT>
+__device__ __forceinline__ void fold_row_tiles(
+    MfmaState<D> (&st)[RT], const u32x4 (&qb)[RT][D / 32], const int (&rows_t)[RT],
+    const int (&pos_first)[RT], const int (&pos_last)[RT], const int (&pos_n)[RT],
+    const u32x4 (&kt)[D / 32], typename MfmaShape<DT, D>::VT (&vt)[4], int limit, int jt,
+    float scale_log2, const MfmaLane& ln) {
+  const int t_first = jt * kBlockSize, t_end = t_first + kBlockSize;
+  u32x2 vb[D / 16];
+  if (limit == kBlockSize)
+    v_operands<DT, D, false>(vt, limit, ln, vb);
+  else
+    v_operands<DT, D, true>(vt, limit, ln, vb);
+  static_for<0, RT>([&](auto rc) __attribute__((always_inline)) {
+    constexpr int r = decltype(rc)::value;
+    if (rows_t[r] == 0 || pos_last[r] < t_first) return;
+    if (limit == kBlockSize && pos_first[r] + 1 >= t_end) {
+      fold_tile<DT, D, false>(st[r], qb[r], kt, vb, limit, scale_log2, ln);
+    } else {
+      const int rl = min(limit, max(0, pos_n[r] + 1 - t_first));
+      fold_tile<DT, D, true>(st[r], qb[r], kt, vb, rl, scale_log2, ln);
+    }
+  });
+}
+
 // Grid: x = KV head + Hkv * unit (the units of one KV head of a sequence read
 // the same tiles; with Hkv a multiple of the 8 XCDs they land on one XCD and
 // share its L2), y = sequence slot (longest context first), z = partition.
 // An item holds RT 16-row tiles: every staged K/V tile is folded into each.
 template <int DT, int D, int NW, int DEPTH, int BS, int RT>
-__global__ __launch_bounds__(NW * 64) void multi_query_kernel(MultiQueryArgs ma) {
+__global__ __launch_bounds__(NW * 64, 2) void multi_query_kernel(MultiQueryArgs ma) {
   using S = MfmaShape<DT, D>;
   using VT = typename S::VT;
   constexpr int EPL = S::EPL;
@@ -72,7 +103,7 @@ __global__ __launch_bounds__(NW * 64) void multi_query_kernel(MultiQueryArgs ma)
   // Row tile r: rows r0 + 16 r + n.  Per lane (row n of each tile) the
   // position of its query token (idle rows take the tile's last row's, so
   // they never narrow the unmasked test) and its q slices.
-  int rows_t[RT], pos_first[RT], pos_n[RT];
+  int rows_t[RT], pos_first[RT], pos_last[RT], pos_n[RT];
   u32x4 qb[RT][S::NJ];
   const u32x4* q = reinterpret_cast<const u32x4*>(a.q);
   static_for<0, RT>([&](auto rc) __attribute__((always_inline)) {
@@ -80,6 +111,7 @@ __global__ __launch_bounds__(NW * 64) void multi_query_kernel(MultiQueryArgs ma)
     const int rb = r0 + 16 * r;
     rows_t[r] = max(0, min(16, rows - 16 * r));
     pos_first[r] = base_pos + rb / G;
+    pos_last[r] = base_pos + (rb + max(rows_t[r] - 1, 0)) / G;
     const bool active = ln.n < rows_t[r];
     const int rn = rb + (active ? ln.n : max(rows_t[r] - 1, 0));
     pos_n[r] = base_pos + rn / G;
@@ -111,22 +143,12 @@ __global__ __launch_bounds__(NW * 64) void multi_query_kernel(MultiQueryArgs ma)
   };
   // (The lambdas here are forced inline: a call would leave everything they
   // capture in scratch memory.)
-  // Stage tile jt's K once, fold it into every live row tile; rows stop at
-  // their own position.  The tests are wave-uniform: every row of a tile
-  // sees the whole K/V tile when its first row does.
+  // Stage tile jt's K once, then fold it into the row tiles.
   auto consume = [&](u32x4 (&kr)[S::NJ], VT (&vr)[4], int limit,
                      int jt) __attribute__((always_inline)) {
     stage_k<D>(kst, kr, ln);
-    static_for<0, RT>([&](auto rc) __attribute__((always_inline)) {
-      constexpr int r = decltype(rc)::value;
-      if (r > 0 && rows_t[r] == 0) return;
-      if (limit == kBlockSize && pos_first[r] + 1 >= (jt + 1) * kBlockSize) {
-        fold_tile<DT, D, false>(st[r], qb[r], kr, vr, limit, limit, a.scale_log2, ln);
-      } else {
-        const int rl = min(limit, max(0, pos_n[r] + 1 - jt * kBlockSize));
-        fold_tile<DT, D, true>(st[r], qb[r], kr, vr, limit, rl, a.scale_log2, ln);
-      }
-    });
+    fold_row_tiles<DT, D, RT>(st, qb, rows_t, pos_first, pos_last, pos_n, kr, vr, limit, jt,
+                              a.scale_log2, ln);
   };
 
   // Software pipeline as in decode: DEPTH register sets, loads issued on
@@ -229,11 +251,181 @@ __global__ __launch_bounds__(NW * 64) void multi_query_kernel(MultiQueryArgs ma)
   });
 }
 
+// LDS of the wide kernel: per buffer and wave, one staged tile (K in the
+// padded staging layout, V as the loading wave's registers) and its token
+// count.
+template <int D, typename VT, int NW>
+struct WideLds {
+  struct Tile {
+    u32x4 k[kKStageSlots<D>];
+    VT v[4][64];
+  };
+  Tile t[2][NW];
+  int lim[2][NW];
+};
+
+// Wide items: many query rows per KV head (long spans, large head groups).
+// Each of the NW waves owns RT 16-row tiles of the item (up to NW * RT * 16
+// rows) and folds every tile of the partition into them; the K/V tiles are
+// loaded once per item, each wave loading one tile of every group of NW,
+// published through double-buffered LDS (one barrier per group) and read by
+// all waves.  A wave's rows are complete in its registers at the end: no
+// merge.
+template <int DT, int D, int NW, int BS, int RT>
+__global__ __launch_bounds__(NW * 64, 2) void multi_query_wide_kernel(MultiQueryArgs ma) {
+  using S = MfmaShape<DT, D>;
+  using VT = typename S::VT;
+  constexpr int EPL = S::EPL;
+  constexpr int ROWS = NW * RT * 16;
+  __shared__ WideLds<D, VT, NW> sm;
+  const DecodeArgs& a = ma.d;
+  const int G = a.num_q_heads / a.num_kv_heads;
+  const int kvh = blockIdx.x % a.num_kv_heads, unit = blockIdx.x / a.num_kv_heads;
+  const int s = longest_first(a, blockIdx.y), part = blockIdx.z;
+  const int L = clamp_len(a, s);
+
+  const int T = ma.num_query_tokens;
+  const int t0 = ma.query_start[s];
+  int nq = ma.query_start[s + 1] - t0;
+  nq = (t0 < 0 || t0 > T) ? 0 : max(0, min(nq, min(ma.max_query_len, T - t0)));
+  const int base_pos = L - nq;
+  if (ma.token_lens != nullptr && kvh == 0 && unit == 0 && part == 0)
+    for (int i = threadIdx.x; i < nq; i += NW * 64) ma.token_lens[t0 + i] = max(base_pos + i + 1, 0);
+
+  const int r0 = unit * ROWS;
+  if (r0 >= nq * G) return;  // past this sequence's rows
+  const int rows = min(ROWS, nq * G - r0);
+  const int span = max(base_pos + (r0 + rows - 1) / G + 1, 0);
+  const int nblocks = (span + kBlockSize - 1) / kBlockSize;
+  if (part >= parts_of(span, a.part_blocks)) return;
+
+  const MfmaLane ln;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // This wave's row tiles: rows r0 + 16 (w RT + r) + n.
+  int rows_t[RT], pos_first[RT], pos_last[RT], pos_n[RT];
+  u32x4 qb[RT][S::NJ];
+  MfmaState<D> st[RT];
+  const u32x4* q = reinterpret_cast<const u32x4*>(a.q);
+  static_for<0, RT>([&](auto rc) __attribute__((always_inline)) {
+    constexpr int r = decltype(rc)::value;
+    const int rb = r0 + 16 * (w * RT + r);
+    rows_t[r] = max(0, min(16, rows - 16 * (w * RT + r)));
+    pos_first[r] = base_pos + rb / G;
+    pos_last[r] = base_pos + (rb + max(rows_t[r] - 1, 0)) / G;
+    const bool active = ln.n < rows_t[r];
+    const int rn = rb + (active ? ln.n : max(rows_t[r] - 1, 0));
+    pos_n[r] = base_pos + rn / G;
+    const int64_t qrow = (int64_t)(t0 + rn / G) * a.num_q_heads + kvh * G + rn % G;
+#pragma unroll
+    for (int jj = 0; jj < S::NJ; ++jj)
+      qb[r][jj] = active ? q[qrow * S::CPR + 4 * jj + ln.g] : u32x4{0u, 0u, 0u, 0u};
+    st[r].reset();
+  });
+
+  const int32_t* __restrict__ bt = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
+  const int jb = part * a.part_blocks;
+  const int je = min(jb + a.part_blocks, nblocks);
+  const int ngroups = je > jb ? (je - jb + NW - 1) / NW : 0;
+  // Tile of group g this wave loads (index clamped into the item).
+  auto id_at = [&](int g) __attribute__((always_inline)) {
+    return tile_ids<BS>(bt, min(jb + g * NW + w, je - 1), a.max_blocks_per_seq);
+  };
+  auto load = [&](int g, const TileIds<BS>& ids, u32x4 (&kr)[S::NJ], VT (&vr)[4],
+                  int& limit) __attribute__((always_inline)) {
+    const int jt = jb + g * NW + w;
+    const bool ok = g < ngroups && jt < je;
+    limit = ok ? tile_limit<BS>(a, ids, span - jt * kBlockSize) : 0;
+    const auto desc = tile_desc<BS, S::TILE_BYTES>(a, ids, jt, kvh, ok);
+    if (ma.reread)
+      load_tile<DT, D, true>(desc, ln, kr, vr);
+    else
+      load_tile<DT, D, false>(desc, ln, kr, vr);
+  };
+
+  if (ngroups > 0) {
+    u32x4 kr[S::NJ];
+    VT vr[4];
+    int lim;
+    load(0, id_at(0), kr, vr, lim);
+    TileIds<BS> next_id = id_at(1);
+    for (int g = 0; g < ngroups; ++g) {
+      const int b = g & 1;
+      // Publish this wave's tile of group g, then start loading group g+1.
+      put_k_stage<D>(sm.t[b][w].k, kr, ln);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sm.t[b][w].v[e][lane] = vr[e];
+      if (lane == 0) sm.lim[b][w] = lim;
+      const TileIds<BS> id = next_id;
+      next_id = id_at(g + 2);
+      load(g + 1, id, kr, vr, lim);
+      __syncthreads();  // group g complete in buffer b (and group g-1's readers done)
+      static_for<0, NW>([&](auto tc) __attribute__((always_inline)) {
+        constexpr int t = decltype(tc)::value;
+        const int jt = jb + g * NW + t;
+        const int limit = __builtin_amdgcn_readfirstlane(sm.lim[b][t]);
+        if (limit == 0) return;
+        u32x4 kt[S::NJ];
+        VT vt[4];
+        get_k_stage<D>(sm.t[b][t].k, kt, ln);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) vt[e] = sm.t[b][t].v[e][lane];
+        fold_row_tiles<DT, D, RT>(st, qb, rows_t, pos_first, pos_last, pos_n, kt, vt, limit,
+                                  jt, a.scale_log2, ln);
+      });
+    }
+  }
+
+  // Each wave writes its own rows: output row 4g+e of a row tile, dims
+  // EPL*n + jj (the P.V result layout).
+  static_for<0, RT>([&](auto rc) __attribute__((always_inline)) {
+    constexpr int r = decltype(rc)::value;
+    if (rows_t[r] == 0) return;
+    const int rb = r0 + 16 * (w * RT + r);
+    float lsum = xor16_combine(st[r].lsum, AddOp{});
+    lsum = xor32_combine(lsum, AddOp{});
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int hh = 4 * ln.g + e;
+      const float lr = u2f((uint32_t)__builtin_amdgcn_ds_bpermute(hh << 2, (int)f2u(lsum)));
+      if (hh >= rows_t[r]) continue;
+      const int R = rb + hh, tok = R / G;
+      const int row_parts = parts_of(max(base_pos + tok + 1, 0), a.part_blocks);
+      if (part >= row_parts) continue;
+      const float inv = lr > 0.f ? 1.f / lr : 0.f;
+      const int64_t orow = (int64_t)(t0 + tok) * a.num_q_heads + kvh * G + R % G;
+      if (row_parts <= 1) {
+#pragma unroll
+        for (int jj = 0; jj < EPL; ++jj)
+          store_elem<DT>(a.out, orow * D + EPL * ln.n + jj, st[r].o[jj][e] * inv);
+      } else {
+        const int64_t prow = orow * a.max_partitions + part;
+#pragma unroll
+        for (int jj = 0; jj < EPL; ++jj) a.tmp_out[prow * D + EPL * ln.n + jj] = st[r].o[jj][e] * inv;
+      }
+    }
+    // per-row max and sum of the partial, from the lanes holding row n
+    if (ln.g == 0 && ln.n < rows_t[r]) {
+      const int R = rb + ln.n, tok = R / G;
+      const int row_parts = parts_of(max(base_pos + tok + 1, 0), a.part_blocks);
+      if (row_parts > 1 && part < row_parts) {
+        const int64_t prow =
+            ((int64_t)(t0 + tok) * a.num_q_heads + kvh * G + R % G) * a.max_partitions + part;
+        a.max_logits[prow] = st[r].m * kLn2;
+        a.exp_sums[prow] = lsum;
+      }
+    }
+  });
+}
+
 template <int DT, int D, int BS>
 hipError_t launch_bs(const MultiQueryArgs& a, hipStream_t stream) {
   const dim3 grid((unsigned)(a.d.num_kv_heads * a.units), (unsigned)a.d.num_seqs,
                   (unsigned)a.d.max_partitions);
-  if (a.row_tiles == 2)
+  if (a.wide)  // two row tiles per wave
+    hipLaunchKernelGGL((multi_query_wide_kernel<DT, D, kMqWaves, BS, 2>), grid,
+                       dim3(kMqWaves * 64), 0, stream, a);
+  else if (a.row_tiles == 2)
     hipLaunchKernelGGL((multi_query_kernel<DT, D, kMqWaves, kMqDepth, BS, 2>), grid,
                        dim3(kMqWaves * 64), 0, stream, a);
   else

@@ -118,7 +118,7 @@ def test_whole_prompts_and_degenerate_spans(cuda):
 
 
 @pytest.mark.parametrize("name,qlen,part", [("llama7b", 4, 0), ("llama7b", 8, 512),
-                                            ("gqa", 4, 0), ("gqa", 8, 512)])
+                                            ("gqa", 4, 0), ("gqa", 8, 512), ("gqa", 16, 0)])
 def test_full_shapes_sampled(cuda, name, qlen, part):
     """The LLaMA-7B (MHA, f16) and GQA (group 8, bf16) decode shapes with
     qlen new tokens per sequence; 96 sampled (token, head) rows, every
