@@ -13,6 +13,10 @@
 
 namespace {
 
+#ifndef PA_MQ_WIDE_ROWS
+#define PA_MQ_WIDE_ROWS 32  // multi-query rows per KV head above which items are wide
+#endif
+
 #ifndef PA_MFMA_MIN_GROUP
 #define PA_MFMA_MIN_GROUP 2  // smallest head group sent to the matrix-core kernel
 #endif
@@ -291,14 +295,15 @@ int pa_paged_attention_multi_query(void* out, const void* q, const void* k_cache
   if (num_seqs == 0 || num_query_tokens == 0 || max_query_len == 0) return PA_OK;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start)
     return PA_ERR_NULL;
-  // Query rows per KV head.  Up to 64: items of one or two 16-row tiles
-  // whose waves split the K/V tiles; more: wide items of 4 waves owning 32
-  // rows each, which share every K/V tile through LDS.
+  // Query rows per KV head.  Up to 16 (32): items of one (two) 16-row
+  // tiles whose 4 waves split the K/V tiles; more: wide items whose 4 waves
+  // own one (up to 64 rows) or two 16-row tiles each and share every K/V
+  // tile through LDS.
   const int64_t rows = std::min<int64_t>(max_query_len, num_query_tokens) *
                        (num_q_heads / num_kv_heads);
-  const int wide = rows > 64 ? 1 : 0;
-  const int row_tiles = wide ? 2 : (rows > 16 ? 2 : 1);
-  const int64_t item_rows = wide ? 4 * 16 * row_tiles : 16 * row_tiles;
+  const int wide = rows > PA_MQ_WIDE_ROWS ? 1 : 0;
+  const int row_tiles = wide ? (rows > 64 ? 2 : 1) : (rows > 16 ? 2 : 1);
+  const int64_t item_rows = (wide ? 4 : 1) * 16 * row_tiles;
   const int64_t units = ceil_div(rows, item_rows);
   if (units * num_kv_heads > INT_MAX) return PA_ERR_SHAPE;
 

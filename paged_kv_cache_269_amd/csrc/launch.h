@@ -57,7 +57,7 @@ struct MultiQueryArgs {
   int max_query_len;           // query tokens per sequence are clamped to this
   int wide;                    // 1: the waves of an item own disjoint row tiles and share
                                //    every K/V tile through LDS; 0: they split the tiles
-  int row_tiles;               // 16-row tiles per item (1 or 2); wide items: 2 per wave
+  int row_tiles;               // 16-row tiles per item, or per wave of a wide item: 1 or 2
   int units;                   // items per KV head
   int reread;                  // 1: K/V tiles are read by several items (cache them)
 };

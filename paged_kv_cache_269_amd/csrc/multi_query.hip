@@ -12,12 +12,17 @@
 //
 // Rows of the matrix-core tile (mfma_tile.h) are (query token, query head)
 // pairs of one KV head, token-major: row R of (sequence, KV head) is token
-// R / G, head kvh * G + R % G.  A 16-row unit streams the K/V tiles up to
-// the position of its last row once; rows whose position ends inside a tile
-// mask the rest of it, and a tile that every row of the unit sees whole goes
-// down the unmasked path.  The NW waves of a workgroup take every NW-th tile
-// and merge through LDS; rows with several partitions leave partials for the
-// log-sum-exp reduce, with each query token's causal length beside them.
+// R / G, head kvh * G + R % G.  An item holds some 16-row tiles of one KV
+// head and streams the K/V tiles up to the position of its last row once;
+// rows whose position ends inside a tile mask the rest of it, and tiles that
+// every row sees whole go down the unmasked path.  Two shapes:
+//   * multi_query_kernel (up to 32 rows per item): the 4 waves take every
+//     4th tile, fold it into all rows, and merge through LDS at the end;
+//   * multi_query_wide_kernel (64 or 128 rows): each wave owns 16 or 32 of
+//     the rows; the K/V tiles are loaded once per item and shared through
+//     LDS, and each wave folds them in runs of several tiles.
+// Rows with several partitions leave partials for the log-sum-exp reduce,
+// with each query token's causal length beside them.
 #include <type_traits>
 
 #include "common.h"
@@ -32,6 +37,10 @@ namespace {
 // Workgroup shape: waves and tiles in flight per wave.
 constexpr int kMqWaves = 4;
 constexpr int kMqDepth = 2;
+#ifndef PA_MQ_FOLD_TILES
+#define PA_MQ_FOLD_TILES 2
+#endif
+constexpr int kFoldTiles = PA_MQ_FOLD_TILES;  // staged tiles folded together (wide items)
 
 // Fold staged tile jt (`limit` tokens) into a wave's RT row tiles, one row
 // tile at a time (folding them side by side needs more registers than two
@@ -264,13 +273,121 @@ struct WideLds {
   int lim[2][NW];
 };
 
+// Fold NT staged tiles (tile t of `tiles`: tokens g_first + 16 t + 0..15,
+// lims[t] of them valid) into a wave's RT row tiles at once: the scores of
+// all NT * 16 tokens first, then one max reduction and one
+// rescale test per row tile, the exponentials, and the P.V products with
+// each tile's V operands built once.  No branch separates the row tiles, so
+// their matrix-core chains interleave.  MASKED: a token counts for row n
+// when it is one of its tile's valid tokens and not past the row's position
+// pos_n; rows that see none of the group add nothing.
+template <int DT, int D, int NT, int RT, bool MASKED, typename Tile>
+__device__ __forceinline__ void fold_group(MfmaState<D> (&st)[RT],
+                                           const u32x4 (&qb)[RT][D / 32],
+                                           const int (&pos_n)[RT], const Tile* tiles,
+                                           const int (&lims)[NT], int g_first,
+                                           float scale_log2, const MfmaLane& ln) {
+  using S = MfmaShape<DT, D>;
+  using VT = typename S::VT;
+  const int lane = ln.n + 16 * ln.g;
+  float sc[RT][NT][4];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    u32x4 kt[S::NJ];
+    get_k_stage<D>(tiles[t].k, kt, ln);
+    f32x4 sacc[RT];
+#pragma unroll
+    for (int r = 0; r < RT; ++r) sacc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int jj = 0; jj < S::NJ; ++jj)
+#pragma unroll
+      for (int r = 0; r < RT; ++r) sacc[r] = mfma_qk<DT>(kt[jj], qb[r][jj], sacc[r]);
+#pragma unroll
+    for (int r = 0; r < RT; ++r)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sc[r][t][e] = sacc[r][e] * scale_log2;
+        if constexpr (MASKED) {
+          const int k = ln.g + 4 * e;
+          const bool ok = k < lims[t] && g_first + kBlockSize * t + k <= pos_n[r];
+          sc[r][t][e] = ok ? sc[r][t][e] : -INFINITY;
+        }
+      }
+  }
+  float mb[RT];
+  bool grow = false;
+#pragma unroll
+  for (int r = 0; r < RT; ++r) {
+    float x = sc[r][0][0];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x = __builtin_fmaxf(x, sc[r][t][e]);
+    mb[r] = xor16_combine(x, MaxOp{});
+  }
+#pragma unroll
+  for (int r = 0; r < RT; ++r) {
+    mb[r] = xor32_combine(mb[r], MaxOp{});
+    grow = grow || mb[r] > st[r].m + kRescaleSlack;
+  }
+  if (__builtin_amdgcn_ballot_w64(grow) != 0) {  // wave-uniform; a rescale to a larger max
+#pragma unroll                                   // never changes the result, so all row
+    for (int r = 0; r < RT; ++r) {               // tiles take it
+      const float mn = __builtin_fmaxf(st[r].m, mb[r]);
+      const float alpha = mn == -INFINITY ? 1.f : fast_exp2(st[r].m - mn);
+      st[r].lsum *= alpha;
+      st[r].m = mn;
+      float arow[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        arow[e] =
+            u2f((uint32_t)__builtin_amdgcn_ds_bpermute((4 * ln.g + e) << 2, (int)f2u(alpha)));
+#pragma unroll
+      for (int jj = 0; jj < S::EPL; ++jj)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) st[r].o[jj][e] *= arow[e];
+    }
+  }
+  u32x2 pa[RT][NT];
+#pragma unroll
+  for (int r = 0; r < RT; ++r) {
+    const bool none = MASKED && st[r].m == -INFINITY;  // no valid token of this row so far
+    float sum = 0.f;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      float p[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        p[e] = fast_exp2(sc[r][t][e] - st[r].m);
+        if constexpr (MASKED) p[e] = none ? 0.f : p[e];
+      }
+      sum += (p[0] + p[1]) + (p[2] + p[3]);
+      pa[r][t] = u32x2{pack2<DT>(p[0], p[1]), pack2<DT>(p[2], p[3])};
+    }
+    st[r].lsum += sum;
+  }
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    VT vt[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) vt[e] = tiles[t].v[e][lane];
+    u32x2 vb[S::EPL];
+    v_operands<DT, D, MASKED>(vt, lims[t], ln, vb);
+#pragma unroll
+    for (int jj = 0; jj < S::EPL; ++jj)
+#pragma unroll
+      for (int r = 0; r < RT; ++r) st[r].o[jj] = mfma_pv<DT>(pa[r][t], vb[jj], st[r].o[jj]);
+  }
+}
+
 // Wide items: many query rows per KV head (long spans, large head groups).
 // Each of the NW waves owns RT 16-row tiles of the item (up to NW * RT * 16
 // rows) and folds every tile of the partition into them; the K/V tiles are
 // loaded once per item, each wave loading one tile of every group of NW,
 // published through double-buffered LDS (one barrier per group) and read by
-// all waves.  A wave's rows are complete in its registers at the end: no
-// merge.
+// all waves, kFoldTiles at a time (fold_group: one max reduction and
+// rescale test per run of tiles, row tiles interleaved).  A wave's rows are
+// complete in its registers at the end: no merge.
 template <int DT, int D, int NW, int BS, int RT>
 __global__ __launch_bounds__(NW * 64, 2) void multi_query_wide_kernel(MultiQueryArgs ma) {
   using S = MfmaShape<DT, D>;
@@ -360,19 +477,31 @@ __global__ __launch_bounds__(NW * 64, 2) void multi_query_wide_kernel(MultiQuery
       next_id = id_at(g + 2);
       load(g + 1, id, kr, vr, lim);
       __syncthreads();  // group g complete in buffer b (and group g-1's readers done)
-      static_for<0, NW>([&](auto tc) __attribute__((always_inline)) {
-        constexpr int t = decltype(tc)::value;
-        const int jt = jb + g * NW + t;
-        const int limit = __builtin_amdgcn_readfirstlane(sm.lim[b][t]);
-        if (limit == 0) return;
-        u32x4 kt[S::NJ];
-        VT vt[4];
-        get_k_stage<D>(sm.t[b][t].k, kt, ln);
+      int lims[NW];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) vt[e] = sm.t[b][t].v[e][lane];
-        fold_row_tiles<DT, D, RT>(st, qb, rows_t, pos_first, pos_last, pos_n, kt, vt, limit,
-                                  jt, a.scale_log2, ln);
-      });
+      for (int t = 0; t < NW; ++t) lims[t] = __builtin_amdgcn_readfirstlane(sm.lim[b][t]);
+      const int g_first = (jb + g * NW) * kBlockSize;  // first token of the group
+      bool any = false, whole = true;
+#pragma unroll
+      for (int t = 0; t < NW; ++t) whole = whole && lims[t] == kBlockSize;
+#pragma unroll
+      for (int r = 0; r < RT; ++r) {
+        any = any || (rows_t[r] > 0 && pos_last[r] >= g_first);
+        whole = whole && (rows_t[r] == 0 || pos_first[r] + 1 >= g_first + NW * kBlockSize);
+      }
+      // the group in runs of FT tiles (registers: FT * 16 scores per row tile)
+      if (any) {
+        static_for<0, NW / kFoldTiles>([&](auto hc) __attribute__((always_inline)) {
+          constexpr int t0 = decltype(hc)::value * kFoldTiles;
+          const int(&lh)[kFoldTiles] = *reinterpret_cast<const int(*)[kFoldTiles]>(&lims[t0]);
+          if (whole)
+            fold_group<DT, D, kFoldTiles, RT, false>(st, qb, pos_n, &sm.t[b][t0], lh,
+                                                     g_first + t0 * kBlockSize, a.scale_log2, ln);
+          else
+            fold_group<DT, D, kFoldTiles, RT, true>(st, qb, pos_n, &sm.t[b][t0], lh,
+                                                    g_first + t0 * kBlockSize, a.scale_log2, ln);
+        });
+      }
     }
   }
 
@@ -422,9 +551,12 @@ template <int DT, int D, int BS>
 hipError_t launch_bs(const MultiQueryArgs& a, hipStream_t stream) {
   const dim3 grid((unsigned)(a.d.num_kv_heads * a.units), (unsigned)a.d.num_seqs,
                   (unsigned)a.d.max_partitions);
-  if (a.wide)  // two row tiles per wave
-    hipLaunchKernelGGL((multi_query_wide_kernel<DT, D, kMqWaves, BS, 2>), grid,
-                       dim3(kMqWaves * 64), 0, stream, a);
+  if (a.wide && a.row_tiles == 2)
+    hipLaunchKernelGGL((multi_query_wide_kernel<DT, D, 4, BS, 2>), grid, dim3(4 * 64), 0, stream,
+                       a);
+  else if (a.wide)
+    hipLaunchKernelGGL((multi_query_wide_kernel<DT, D, 4, BS, 1>), grid, dim3(4 * 64), 0, stream,
+                       a);
   else if (a.row_tiles == 2)
     hipLaunchKernelGGL((multi_query_kernel<DT, D, kMqWaves, kMqDepth, BS, 2>), grid,
                        dim3(kMqWaves * 64), 0, stream, a);

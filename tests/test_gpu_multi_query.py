@@ -3,11 +3,11 @@
 Each sequence's last n_s context tokens are queries; token i of a span
 attends to tokens 0 .. L - n + i.  Cases: spans of 1 (decode), ragged spans
 that cross tile and block boundaries, whole prompts (n = L), an empty span,
-spans longer than the context (leading rows attend to nothing), head groups
-1 to 16 (1 to 3 row units per KV head), block sizes 8/16/32, one pass and
-several partition sizes (the log-sum-exp reduce with per-token causal
-lengths), and the LLaMA-7B and GQA decode shapes with 4 and 8 new tokens
-per sequence, sampled.
+spans longer than the context (leading rows attend to nothing), chunks of
+33-128 tokens, head groups 1 to 16 (both item shapes, several items per KV
+head), block sizes 8/16/32, one pass and several partition sizes (the
+log-sum-exp reduce with per-token causal lengths), and the LLaMA-7B and GQA
+decode shapes with 4, 8 and 16 new tokens per sequence, sampled.
 """
 import sys
 
@@ -115,6 +115,22 @@ def test_whole_prompts_and_degenerate_spans(cuda):
         got = to_f64(run_mq(run, spans, cuda, part), "f16")
         check_close(got, ref, "f16", f"whole prompts partition {part}")
         assert not got[qs[4]:qs[4] + 2].any() and not got[qs[5]:qs[5] + 4].any()
+
+
+@pytest.mark.parametrize("G,part", [(8, 0), (8, 64), (2, 0)])
+def test_long_spans_chunked_prefill(cuda, G, part):
+    """Chunks of 33 to 128 new tokens (a whole 128-token prompt among them):
+    several wide items per KV head whose rows end in different tiles, so
+    groups of tiles are partly visible to a row tile and the first tiles of
+    a group are past some rows' positions."""
+    announce("multi-query long spans", G, part)
+    lens, nqs = [300, 128, 700, 45], [64, 128, 33, 40]
+    w, run = prepared(cuda, dtype="bf16", head_dim=128, num_kv_heads=1, num_q_heads=G,
+                      lens=lens, seed=98)
+    spans = W.generate_query_spans(w, nqs, seed=99)
+    ref = oracle_mq(w, spans)
+    got = to_f64(run_mq(run, spans, cuda, part), "bf16")
+    check_close(got, ref, "bf16", f"long spans G{G} partition {part}")
 
 
 @pytest.mark.parametrize("name,qlen,part", [("llama7b", 4, 0), ("llama7b", 8, 512),
