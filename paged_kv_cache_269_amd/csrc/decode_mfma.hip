@@ -487,6 +487,12 @@ __global__ __launch_bounds__(NW * 64, PA_STREAM_MIN_WAVES) void decode_mfma_stre
 // Launch shapes: items of at least kLongItemBlocks blocks get 8 waves,
 // shorter ones 4 (more workgroups resident per CU).
 constexpr int kLongItemBlocks = 128;
+#ifndef PA_MFMA_LONG_WAVES
+#define PA_MFMA_LONG_WAVES 8
+#endif
+#ifndef PA_MFMA_LONG_DEPTH
+#define PA_MFMA_LONG_DEPTH 2
+#endif
 
 template <int DT, int D, int NW, int DEPTH, int BS = kBlockSize>
 hipError_t launch_shape(const DecodeArgs& a, hipStream_t stream) {
@@ -562,8 +568,9 @@ hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
     return launch_stream_shape<DT, D, PA_MFMA_STREAM_WAVES, PA_MFMA_STREAM_DEPTH>(a, items, stream);
   if (a.max_partitions >= kWaveItemParts)
     return launch_wave_shape<DT, D, PA_MFMA_WAVE_ITEM_WAVES, PA_MFMA_WAVE_ITEM_DEPTH>(a, stream);
-  return a.part_blocks >= kLongItemBlocks ? launch_shape<DT, D, 8, 2>(a, stream)
-                                          : launch_shape<DT, D, 4, 2>(a, stream);
+  return a.part_blocks >= kLongItemBlocks
+             ? launch_shape<DT, D, PA_MFMA_LONG_WAVES, PA_MFMA_LONG_DEPTH>(a, stream)
+             : launch_shape<DT, D, 4, 2>(a, stream);
 }
 
 }  // namespace

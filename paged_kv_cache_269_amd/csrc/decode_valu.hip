@@ -303,10 +303,12 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_wave_kernel(DecodeArgs a)
 #define PA_WAVE_ITEM_DEPTH 3  // tiles per wave in the load pipeline, one-wave items
 #endif
 
-// Launch shapes: items of at least kLongItemBlocks blocks get 8 waves and a
-// 3-deep load pipeline (more bytes in flight per item); shorter items get 4
-// waves and 2 tiles in flight, which keeps more workgroups resident per CU.
-constexpr int kLongItemBlocks = 128;
+// Workgroup-per-item launches: 4 waves, 2 tiles in flight per wave.  On the
+// LLaMA-7B shape (items of 32-128 blocks) this measured 201 us per call
+// against 206-209 us for 8 waves with 3 tiles in flight, and 203-205 us for
+// 8 x 2, 4 x 3 and 4 x 4: more, smaller workgroups per CU balance better.
+constexpr int kItemWaves = 4;
+constexpr int kItemDepth = 2;
 
 template <int DT, int D, int NW, int DEPTH, int BS = kBlockSize>
 hipError_t launch_shape(const DecodeArgs& a, hipStream_t stream) {
@@ -340,18 +342,13 @@ hipError_t launch_wave_shape(const DecodeArgs& a, hipStream_t stream) {
 template <int DT, int D>
 hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
   // 8- and 32-token blocks: workgroup-per-item kernels for every launch.
-  if (a.block_size == 8)
-    return a.part_blocks >= kLongItemBlocks ? launch_shape<DT, D, 8, 3, 8>(a, stream)
-                                            : launch_shape<DT, D, 4, 2, 8>(a, stream);
-  if (a.block_size == 32)
-    return a.part_blocks >= kLongItemBlocks ? launch_shape<DT, D, 8, 3, 32>(a, stream)
-                                            : launch_shape<DT, D, 4, 2, 32>(a, stream);
+  if (a.block_size == 8) return launch_shape<DT, D, kItemWaves, kItemDepth, 8>(a, stream);
+  if (a.block_size == 32) return launch_shape<DT, D, kItemWaves, kItemDepth, 32>(a, stream);
   // After a shared-prefix pass the items hold only the private blocks.
   if (a.prefix_blocks != nullptr)
     return launch_shape<DT, D, PA_CASCADE_WAVES, PA_CASCADE_DEPTH>(a, stream);
   if (a.max_partitions >= kWaveItemParts) return launch_wave_shape<DT, D, PA_WAVE_ITEM_WAVES, PA_WAVE_ITEM_DEPTH>(a, stream);
-  return a.part_blocks >= kLongItemBlocks ? launch_shape<DT, D, 8, 3>(a, stream)
-                                          : launch_shape<DT, D, 4, 2>(a, stream);
+  return launch_shape<DT, D, kItemWaves, kItemDepth>(a, stream);
 }
 
 }  // namespace
