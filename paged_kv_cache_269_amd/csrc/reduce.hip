@@ -8,11 +8,13 @@
 // partitions processed in parallel; it runs after the decode kernel on the
 // same stream.
 //
-// One workgroup (512 lanes) per (query head, sequence): the weights of up to
-// 512 partitions at a time go to LDS, then 512 / head_dim lane groups each
-// sweep a share of those partitions over all head_dim columns (coalesced
-// reads of tmp_out rows, kUnroll independent loads in flight per lane), and
-// the shares are added at the end.
+// One workgroup (512 lanes) per (query head, sequence): of up to 512
+// partitions at a time, those with weight are compacted into LDS (index and
+// weight; slots left empty by a kernel that folded several partitions into
+// one are never read), then 512 / head_dim lane groups each sweep a share of
+// them over all head_dim columns (coalesced reads of tmp_out rows, kUnroll
+// independent loads in flight per lane), and the shares are added at the
+// end.
 #include "common.h"
 #include "launch.h"
 
@@ -48,6 +50,8 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(ReduceArgs a) {
   const int64_t base = orow * a.max_partitions;
 
   __shared__ float s_w[kThreads];
+  __shared__ int s_p[kThreads];
+  __shared__ int s_cnt[kThreads / 64];
   __shared__ float s_red[kThreads / 64];
   __shared__ float s_o[SPLIT][D];
   __shared__ float s_ws[SPLIT];
@@ -60,6 +64,7 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(ReduceArgs a) {
   const float M = block_max(mx, s_red);
 
   const int d = tid % D, share = tid / D;
+  const int lane = tid & 63, wave = tid >> 6;
   float o = 0.f, wsum = 0.f;
   for (int p0 = 0; p0 < P; p0 += kThreads) {
     const int p = p0 + tid;
@@ -68,23 +73,39 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(ReduceArgs a) {
       const float l = a.exp_sums[base + p];
       if (l > 0.f) wv = l * fast_exp2((a.max_logits[base + p] - M) * kLog2e);
     }
-    s_w[tid] = wv;
+    // Compact the partitions with weight into s_w / s_p (in partition
+    // order): weightless ones -- the empty slots of folded partitions --
+    // are not read at all.
+    const uint64_t has = __builtin_amdgcn_ballot_w64(wv > 0.f);
+    if (lane == 0) s_cnt[wave] = __builtin_popcountll(has);
     __syncthreads();
-    const int cnt = min(kThreads, P - p0);
+    int before = 0, cnt = 0;
+#pragma unroll
+    for (int i = 0; i < kThreads / 64; ++i) {
+      before += i < wave ? s_cnt[i] : 0;
+      cnt += s_cnt[i];
+    }
+    if (wv > 0.f) {
+      const int k = before + __builtin_amdgcn_mbcnt_hi((uint32_t)(has >> 32),
+                                                       __builtin_amdgcn_mbcnt_lo((uint32_t)has, 0));
+      s_w[k] = wv;
+      s_p[k] = p;
+    }
+    __syncthreads();
     for (int k = share; k < cnt; k += SPLIT * kUnroll) {
-      float t[kUnroll], wv[kUnroll];
+      float t[kUnroll], wk[kUnroll];
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {  // loads issued unconditionally (index kept in range)
         const int kk = k + u * SPLIT;
         const bool in = kk < cnt;
         const int ki = in ? kk : share;
-        wv[u] = in ? s_w[ki] : 0.f;
-        t[u] = a.tmp_out[(base + p0 + ki) * D + d];
+        wk[u] = in ? s_w[ki] : 0.f;
+        t[u] = a.tmp_out[(base + s_p[ki]) * D + d];
       }
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
-        wsum += wv[u];
-        o += wv[u] != 0.f ? wv[u] * t[u] : 0.f;  // a weightless row may hold anything
+        wsum += wk[u];
+        o += wk[u] * t[u];
       }
     }
     __syncthreads();
