@@ -275,12 +275,12 @@ struct WideLds {
 
 // Fold NT staged tiles (tile t of `tiles`: tokens g_first + 16 t + 0..15,
 // lims[t] of them valid) into a wave's RT row tiles at once: the scores of
-// all NT * 16 tokens first, then one max reduction and one
-// rescale test per row tile, the exponentials, and the P.V products with
-// each tile's V operands built once.  No branch separates the row tiles, so
-// their matrix-core chains interleave.  MASKED: a token counts for row n
-// when it is one of its tile's valid tokens and not past the row's position
-// pos_n; rows that see none of the group add nothing.
+// all NT * 16 tokens first, then one max reduction and one rescale test per
+// row tile, the exponentials, and the P.V products -- over pairs of tiles
+// as 16x16x32 products where registers allow.  No branch separates the row
+// tiles, so their matrix-core chains interleave.  MASKED: a token counts for
+// row n when it is one of its tile's valid tokens and not past the row's
+// position pos_n; rows that see none of the group add nothing.
 template <int DT, int D, int NT, int RT, bool MASKED, typename Tile>
 __device__ __forceinline__ void fold_group(MfmaState<D> (&st)[RT],
                                            const u32x4 (&qb)[RT][D / 32],
@@ -366,17 +366,61 @@ __device__ __forceinline__ void fold_group(MfmaState<D> (&st)[RT],
     }
     st[r].lsum += sum;
   }
+  // P.V over pairs of tiles: the two tiles' 4 + 4 tokens of a lane are one
+  // 8-wide contraction slice of a 16x16x32 product (P and V take the tokens
+  // in the same order), half the instructions of two 16x16x16 products.
+  // The V rows are read from LDS in 8-byte halves of the lane's slices
+  // (D = 128: dims EPL*n + 0..3, then + 4..7), which keeps half the V
+  // registers live.  Two 32-row tiles at D = 128 leave no registers for the
+  // pair's operands (measured: spilling made it slower than per-tile
+  // 16x16x16 products), so that shape keeps the per-tile products.
+  constexpr bool PAIRS = NT % 2 == 0 && (RT == 1 || D <= 64);
+  if constexpr (!PAIRS) {
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    VT vt[4];
+    for (int t = 0; t < NT; ++t) {
+      VT vt[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) vt[e] = tiles[t].v[e][lane];
-    u32x2 vb[S::EPL];
-    v_operands<DT, D, MASKED>(vt, lims[t], ln, vb);
+      for (int e = 0; e < 4; ++e) vt[e] = tiles[t].v[e][lane];
+      u32x2 vb[S::EPL];
+      v_operands<DT, D, MASKED>(vt, lims[t], ln, vb);
 #pragma unroll
-    for (int jj = 0; jj < S::EPL; ++jj)
+      for (int jj = 0; jj < S::EPL; ++jj)
 #pragma unroll
-      for (int r = 0; r < RT; ++r) st[r].o[jj] = mfma_pv<DT>(pa[r][t], vb[jj], st[r].o[jj]);
+        for (int r = 0; r < RT; ++r) st[r].o[jj] = mfma_pv<DT>(pa[r][t], vb[jj], st[r].o[jj]);
+    }
+  } else {
+    constexpr int HALVES = S::EPL / 4;
+#pragma unroll
+    for (int t = 0; t < NT; t += 2) {
+      u32x4 pp[RT];
+#pragma unroll
+      for (int r = 0; r < RT; ++r)
+        pp[r] = u32x4{pa[r][t][0], pa[r][t][1], pa[r][t + 1][0], pa[r][t + 1][1]};
+#pragma unroll
+      for (int hv = 0; hv < HALVES; ++hv) {
+        u32x2 v0[4], v1[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v0[e] = reinterpret_cast<const u32x2*>(&tiles[t].v[e][lane])[hv];
+          v1[e] = reinterpret_cast<const u32x2*>(&tiles[t + 1].v[e][lane])[hv];
+          if constexpr (MASKED) {
+            // what the slots past a tile's tokens hold must not reach P.V
+            if (ln.g + 4 * e >= lims[t]) v0[e] = u32x2{0u, 0u};
+            if (ln.g + 4 * e >= lims[t + 1]) v1[e] = u32x2{0u, 0u};
+          }
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int jj = 4 * hv + k;
+          const u32x4 vb{VSlice<4>::half(v0[0], k) | (VSlice<4>::half(v0[1], k) << 16),
+                         VSlice<4>::half(v0[2], k) | (VSlice<4>::half(v0[3], k) << 16),
+                         VSlice<4>::half(v1[0], k) | (VSlice<4>::half(v1[1], k) << 16),
+                         VSlice<4>::half(v1[2], k) | (VSlice<4>::half(v1[3], k) << 16)};
+#pragma unroll
+          for (int r = 0; r < RT; ++r) st[r].o[jj] = mfma_qk<DT>(pp[r], vb, st[r].o[jj]);
+        }
+      }
+    }
   }
 }
 
