@@ -37,10 +37,7 @@ namespace {
 // Workgroup shape: waves and tiles in flight per wave.
 constexpr int kMqWaves = 4;
 constexpr int kMqDepth = 2;
-#ifndef PA_MQ_FOLD_TILES
-#define PA_MQ_FOLD_TILES 2
-#endif
-constexpr int kFoldTiles = PA_MQ_FOLD_TILES;  // staged tiles folded together (wide items)
+constexpr int kFoldTiles = 2;  // staged tiles folded together (wide items)
 
 // Fold staged tile jt (`limit` tokens) into a wave's RT row tiles, one row
 // tile at a time (folding them side by side needs more registers than two
@@ -266,18 +263,42 @@ __global__ __launch_bounds__(NW * 64, 2) void multi_query_kernel(MultiQueryArgs 
 template <int D, typename VT, int NW>
 struct WideLds {
   struct Tile {
-    u32x4 k[kKStageSlots<D>];
-    VT v[4][64];
+    u32x4 k[kBlockSize * D / 8];  // 16-byte chunk c of row r at r * D/8 + (c ^ r % (D/8))
+    VT v[4][64];                  // rows in order: lane l's V slice of rows g + 4e at [e][l]
   };
   Tile t[2][NW];
   int lim[2][NW];
 };
 
+// Position of K chunk c of token row r in a wide tile: chunks are permuted
+// within each row so that the S operand reads (16 rows, one chunk each, for
+// one contraction slice) fall on distinct banks.
+template <int D>
+__device__ __forceinline__ int kswz(int r, int c) {
+  constexpr int CPR = D / 8;
+  return r * CPR + (c ^ (r % CPR));
+}
+
+// 16-byte buffer load of each lane straight into LDS: lane l writes the
+// 16 bytes at dst + 16 l (dst wave-uniform).  The builtin exists only for
+// the device pass; the host pass (which instantiates the kernel templates
+// for their launch stubs) sees an empty body.
+template <int AUX>
+__device__ __forceinline__ void load16_to_lds(Rsrc r, u32x4* dst, int voffset) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16,
+                                           voffset, 0, 0, AUX);
+#endif
+}
+
+// Wait for this wave's loads into LDS to land.
+__device__ __forceinline__ void wait_lds_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 // Fold NT staged tiles (tile t of `tiles`: tokens g_first + 16 t + 0..15,
 // lims[t] of them valid) into a wave's RT row tiles at once: the scores of
 // all NT * 16 tokens first, then one max reduction and one rescale test per
 // row tile, the exponentials, and the P.V products -- over pairs of tiles
-// as 16x16x32 products where registers allow.  No branch separates the row
+// as 16x16x32 products.  No branch separates the row
 // tiles, so their matrix-core chains interleave.  MASKED: a token counts for
 // row n when it is one of its tile's valid tokens and not past the row's
 // position pos_n; rows that see none of the group add nothing.
@@ -294,7 +315,8 @@ __device__ __forceinline__ void fold_group(MfmaState<D> (&st)[RT],
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     u32x4 kt[S::NJ];
-    get_k_stage<D>(tiles[t].k, kt, ln);
+#pragma unroll
+    for (int jj = 0; jj < S::NJ; ++jj) kt[jj] = tiles[t].k[kswz<D>(ln.tok_k, 4 * jj + ln.g)];
     f32x4 sacc[RT];
 #pragma unroll
     for (int r = 0; r < RT; ++r) sacc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -371,54 +393,37 @@ __device__ __forceinline__ void fold_group(MfmaState<D> (&st)[RT],
   // in the same order), half the instructions of two 16x16x16 products.
   // The V rows are read from LDS in 8-byte halves of the lane's slices
   // (D = 128: dims EPL*n + 0..3, then + 4..7), which keeps half the V
-  // registers live.  Two 32-row tiles at D = 128 leave no registers for the
-  // pair's operands (measured: spilling made it slower than per-tile
-  // 16x16x16 products), so that shape keeps the per-tile products.
-  constexpr bool PAIRS = NT % 2 == 0 && (RT == 1 || D <= 64);
-  if constexpr (!PAIRS) {
+  // registers live.
+  static_assert(NT % 2 == 0, "tiles are folded in pairs");
+  constexpr int HALVES = S::EPL / 4;
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      VT vt[4];
+  for (int t = 0; t < NT; t += 2) {
+    u32x4 pp[RT];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) vt[e] = tiles[t].v[e][lane];
-      u32x2 vb[S::EPL];
-      v_operands<DT, D, MASKED>(vt, lims[t], ln, vb);
+    for (int r = 0; r < RT; ++r)
+      pp[r] = u32x4{pa[r][t][0], pa[r][t][1], pa[r][t + 1][0], pa[r][t + 1][1]};
 #pragma unroll
-      for (int jj = 0; jj < S::EPL; ++jj)
+    for (int hv = 0; hv < HALVES; ++hv) {
+      u32x2 v0[4], v1[4];
 #pragma unroll
-        for (int r = 0; r < RT; ++r) st[r].o[jj] = mfma_pv<DT>(pa[r][t], vb[jj], st[r].o[jj]);
-    }
-  } else {
-    constexpr int HALVES = S::EPL / 4;
-#pragma unroll
-    for (int t = 0; t < NT; t += 2) {
-      u32x4 pp[RT];
-#pragma unroll
-      for (int r = 0; r < RT; ++r)
-        pp[r] = u32x4{pa[r][t][0], pa[r][t][1], pa[r][t + 1][0], pa[r][t + 1][1]};
-#pragma unroll
-      for (int hv = 0; hv < HALVES; ++hv) {
-        u32x2 v0[4], v1[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          v0[e] = reinterpret_cast<const u32x2*>(&tiles[t].v[e][lane])[hv];
-          v1[e] = reinterpret_cast<const u32x2*>(&tiles[t + 1].v[e][lane])[hv];
-          if constexpr (MASKED) {
-            // what the slots past a tile's tokens hold must not reach P.V
-            if (ln.g + 4 * e >= lims[t]) v0[e] = u32x2{0u, 0u};
-            if (ln.g + 4 * e >= lims[t + 1]) v1[e] = u32x2{0u, 0u};
-          }
+      for (int e = 0; e < 4; ++e) {
+        v0[e] = reinterpret_cast<const u32x2*>(&tiles[t].v[e][lane])[hv];
+        v1[e] = reinterpret_cast<const u32x2*>(&tiles[t + 1].v[e][lane])[hv];
+        if constexpr (MASKED) {
+          // what the slots past a tile's tokens hold must not reach P.V
+          if (ln.g + 4 * e >= lims[t]) v0[e] = u32x2{0u, 0u};
+          if (ln.g + 4 * e >= lims[t + 1]) v1[e] = u32x2{0u, 0u};
         }
+      }
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int jj = 4 * hv + k;
-          const u32x4 vb{VSlice<4>::half(v0[0], k) | (VSlice<4>::half(v0[1], k) << 16),
-                         VSlice<4>::half(v0[2], k) | (VSlice<4>::half(v0[3], k) << 16),
-                         VSlice<4>::half(v1[0], k) | (VSlice<4>::half(v1[1], k) << 16),
-                         VSlice<4>::half(v1[2], k) | (VSlice<4>::half(v1[3], k) << 16)};
+      for (int k = 0; k < 4; ++k) {
+        const int jj = 4 * hv + k;
+        const u32x4 vb{VSlice<4>::half(v0[0], k) | (VSlice<4>::half(v0[1], k) << 16),
+                       VSlice<4>::half(v0[2], k) | (VSlice<4>::half(v0[3], k) << 16),
+                       VSlice<4>::half(v1[0], k) | (VSlice<4>::half(v1[1], k) << 16),
+                       VSlice<4>::half(v1[2], k) | (VSlice<4>::half(v1[3], k) << 16)};
 #pragma unroll
-          for (int r = 0; r < RT; ++r) st[r].o[jj] = mfma_qk<DT>(pp[r], vb, st[r].o[jj]);
-        }
+        for (int r = 0; r < RT; ++r) st[r].o[jj] = mfma_qk<DT>(pp[r], vb, st[r].o[jj]);
       }
     }
   }
@@ -427,10 +432,11 @@ __device__ __forceinline__ void fold_group(MfmaState<D> (&st)[RT],
 // Wide items: many query rows per KV head (long spans, large head groups).
 // Each of the NW waves owns RT 16-row tiles of the item (up to NW * RT * 16
 // rows) and folds every tile of the partition into them; the K/V tiles are
-// loaded once per item, each wave loading one tile of every group of NW,
-// published through double-buffered LDS (one barrier per group) and read by
-// all waves, kFoldTiles at a time (fold_group: one max reduction and
-// rescale test per run of tiles, row tiles interleaved).  A wave's rows are
+// loaded once per item, each wave loading one tile of every group of NW
+// straight into double-buffered LDS (buffer loads with the LDS destination:
+// no registers hold tiles in flight; one barrier per group), and read by
+// all waves kFoldTiles at a time (fold_group: one max reduction and rescale
+// test per run of tiles, row tiles interleaved).  A wave's rows are
 // complete in its registers at the end: no merge.
 template <int DT, int D, int NW, int BS, int RT>
 __global__ __launch_bounds__(NW * 64, 2) void multi_query_wide_kernel(MultiQueryArgs ma) {
@@ -492,35 +498,50 @@ __global__ __launch_bounds__(NW * 64, 2) void multi_query_wide_kernel(MultiQuery
   auto id_at = [&](int g) __attribute__((always_inline)) {
     return tile_ids<BS>(bt, min(jb + g * NW + w, je - 1), a.max_blocks_per_seq);
   };
-  auto load = [&](int g, const TileIds<BS>& ids, u32x4 (&kr)[S::NJ], VT (&vr)[4],
-                  int& limit) __attribute__((always_inline)) {
+  // This wave's tile of group g into LDS buffer `b`, with its token count.
+  u32x4* const lds_k[2] = {sm.t[0][w].k, sm.t[1][w].k};
+  u32x4* const lds_v[2] = {reinterpret_cast<u32x4*>(sm.t[0][w].v),
+                           reinterpret_cast<u32x4*>(sm.t[1][w].v)};
+  int* const lds_lim[2] = {&sm.lim[0][w], &sm.lim[1][w]};
+  auto load = [&](int g, const TileIds<BS>& ids, int b) __attribute__((always_inline)) {
     const int jt = jb + g * NW + w;
     const bool ok = g < ngroups && jt < je;
-    limit = ok ? tile_limit<BS>(a, ids, span - jt * kBlockSize) : 0;
-    const auto desc = tile_desc<BS, S::TILE_BYTES>(a, ids, jt, kvh, ok);
-    if (ma.reread)
-      load_tile<DT, D, true>(desc, ln, kr, vr);
-    else
-      load_tile<DT, D, false>(desc, ln, kr, vr);
+    const int limit = ok ? tile_limit<BS>(a, ids, span - jt * kBlockSize) : 0;
+    const TileDesc<BS, S::TILE_BYTES> desc = tile_desc<BS, S::TILE_BYTES>(a, ids, jt, kvh, ok);
+    // Buffer loads with the LDS destination: lane l of a load writes the 16
+    // bytes at slot 64 jj + l of the load's KiB, no registers involved.  A K
+    // load's lane fetches the chunk kswz puts at its slot; V keeps row order.
+    // Which block part a load reads is known at compile time, as in load_tile.
+    using Desc = TileDesc<BS, S::TILE_BYTES>;
+    static_for<0, S::NJ>([&](auto jc) __attribute__((always_inline)) {
+      constexpr int jj = decltype(jc)::value;
+      constexpr int h = Desc::part(jj * 1024);
+      const int p = jj * 64 + lane;
+      const int r = p / S::CPR, c = (p % S::CPR) ^ (r % S::CPR);
+      const int koff = (r * S::CPR + c) * 16 - h * Desc::HB, voff = p * 16 - h * Desc::HB;
+      if (ma.reread) {
+        load16_to_lds<PA_SHARED_LOAD_POLICY>(desc.k[h], lds_k[b] + jj * 64, koff);
+        load16_to_lds<PA_SHARED_LOAD_POLICY>(desc.v[h], lds_v[b] + jj * 64, voff);
+      } else {
+        load16_to_lds<PA_KV_LOAD_POLICY>(desc.k[h], lds_k[b] + jj * 64, koff);
+        load16_to_lds<PA_KV_LOAD_POLICY>(desc.v[h], lds_v[b] + jj * 64, voff);
+      }
+    });
+    if (lane == 0) *lds_lim[b] = limit;
   };
 
   if (ngroups > 0) {
-    u32x4 kr[S::NJ];
-    VT vr[4];
-    int lim;
-    load(0, id_at(0), kr, vr, lim);
+    // Group g + 1 streams into the other buffer while group g is folded;
+    // a wait for the wave's own loads and one barrier per group.
+    load(0, id_at(0), 0);
     TileIds<BS> next_id = id_at(1);
+    wait_lds_loads();
+    __syncthreads();
     for (int g = 0; g < ngroups; ++g) {
       const int b = g & 1;
-      // Publish this wave's tile of group g, then start loading group g+1.
-      put_k_stage<D>(sm.t[b][w].k, kr, ln);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) sm.t[b][w].v[e][lane] = vr[e];
-      if (lane == 0) sm.lim[b][w] = lim;
       const TileIds<BS> id = next_id;
       next_id = id_at(g + 2);
-      load(g + 1, id, kr, vr, lim);
-      __syncthreads();  // group g complete in buffer b (and group g-1's readers done)
+      load(g + 1, id, b ^ 1);  // buffer b ^ 1 was last read before the previous barrier
       int lims[NW];
 #pragma unroll
       for (int t = 0; t < NW; ++t) lims[t] = __builtin_amdgcn_readfirstlane(sm.lim[b][t]);
@@ -546,6 +567,8 @@ __global__ __launch_bounds__(NW * 64, 2) void multi_query_wide_kernel(MultiQuery
                                                     g_first + t0 * kBlockSize, a.scale_log2, ln);
         });
       }
+      wait_lds_loads();
+      __syncthreads();  // group g + 1 in buffer b ^ 1; every wave done with buffer b
     }
   }
 
