@@ -227,6 +227,23 @@ def test_library_append_batch_matches_sequential_appends(hiplib):
     lib.close()
 
 
+def test_reference_copy_blocks_hand_example():
+    """Copy-on-write copies on a 5-block pool whose blocks hold their own id
+    (K) and minus their id (V), every KV head and row: pairs (1 -> 3) and
+    (0 -> 4) leave blocks 0, 1, 2 as they were and make 3 and 4 copies of
+    1 and 0, in both caches."""
+    from oracle.block_manager import copy_blocks
+    N, Hkv, bs, D = 5, 2, 4, 3
+    k = np.repeat(np.arange(N, dtype=np.float32), Hkv * bs * D).reshape(N, Hkv, bs, D)
+    v = -k.copy()
+    copy_blocks(k, v, [(1, 3), (0, 4)])
+    assert [float(k[b, 0, 0, 0]) for b in range(N)] == [0, 1, 2, 1, 0]
+    assert [float(v[b, 1, 3, 2]) for b in range(N)] == [0, -1, -2, -1, 0]
+    assert (k == k[:, :1, :1, :1]).all() and (v == v[:, :1, :1, :1]).all()   # whole blocks
+    copy_blocks(k, v, np.zeros((0, 2), np.int64))                          # no pairs: no change
+    assert [float(k[b, 1, 2, 1]) for b in range(N)] == [0, 1, 2, 1, 0]
+
+
 def test_copy_validator(hiplib):
     ok = np.array([[0, 5], [1, 6], [0, 7]])
     assert hiplib.validate_copy_host(ok, 8) == 0
