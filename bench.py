@@ -293,6 +293,11 @@ def block_ops(w, dev):
     out_us = timed(lambda: pa.swap_blocks(kc, host, out_pairs))
     in_us = timed(lambda: pa.swap_blocks(host, kc, in_pairs))
     sw_bytes = 1024 * block_bytes
+    # the same moves in one kernel through the pinned buffer's device mapping
+    out_p = torch.from_numpy(np.ascontiguousarray(out_pairs, dtype=np.int64)).to(dev)
+    in_p = torch.from_numpy(np.ascontiguousarray(in_pairs, dtype=np.int64)).to(dev)
+    mout_us = timed(lambda: pa.swap_blocks_mapped(kc, host, out_p))
+    min_us = timed(lambda: pa.swap_blocks_mapped(host, kc, in_p))
     return {"block_bytes_per_cache": block_bytes,
             "copy_pairs": 2048, "copy_us": round(copy_us, 2),
             "copy_GBps": round(copy_bytes / copy_us / 1e3, 1),
@@ -300,8 +305,12 @@ def block_ops(w, dev):
             "swap_blocks": 1024, "swap_out_us": round(out_us, 1), "swap_in_us": round(in_us, 1),
             "swap_out_GBps": round(sw_bytes / out_us / 1e3, 1),
             "swap_in_GBps": round(sw_bytes / in_us / 1e3, 1),
+            "swap_mapped_out_us": round(mout_us, 1), "swap_mapped_in_us": round(min_us, 1),
+            "swap_mapped_out_GBps": round(sw_bytes / mout_us / 1e3, 1),
+            "swap_mapped_in_GBps": round(sw_bytes / min_us / 1e3, 1),
             "note": "copy: read + write of K and V blocks; swap: one cache, scattered blocks, "
-                    "one asynchronous copy each"}
+                    "one asynchronous copy each; swap_mapped: one kernel through the pinned "
+                    "buffer's device mapping"}
 
 
 def multi_query_bench(args, w, d, pools, part, stream):

@@ -283,6 +283,23 @@ int pa_swap_blocks(const void* src_cache, void* dst_cache, const int64_t* block_
                    int32_t num_pairs, int64_t block_bytes, void* stream);
 
 /*
+ * The same block moves as pa_swap_blocks, done by one kernel instead of a
+ * copy per block: for every pair i, block_bytes bytes at block
+ * block_pairs[2i] of src_cache go to block block_pairs[2i+1] of dst_cache.
+ * Either cache may be pinned host memory (the kernel reaches it through its
+ * device mapping) or device memory; block_pairs [num_pairs, 2] int64 must
+ * be device memory or pinned host memory too.  Pointers the device cannot
+ * reach (pageable host memory) give PA_ERR_UNSUPPORTED before anything is
+ * launched, as do caches not 16-byte aligned.  Pairs naming a block outside
+ * [0, src_blocks) or [0, dst_blocks) are skipped.  block_bytes a positive
+ * multiple of 16; num_pairs <= 65535; 0 is a no-op.  Destinations must be
+ * distinct (a caller error otherwise).
+ */
+int pa_swap_blocks_mapped(const void* src_cache, void* dst_cache, const int64_t* block_pairs,
+                          int32_t num_pairs, int64_t block_bytes, int64_t src_blocks,
+                          int64_t dst_blocks, void* stream);
+
+/*
  * Host check of copy pairs (host pointer): ids in [0, num_blocks), distinct
  * destinations, no destination used as a source.  PA_OK or PA_ERR_RANGE.
  */

@@ -26,6 +26,7 @@ from ._binding import (  # noqa: F401
     reshape_and_cache,
     status_string,
     swap_blocks,
+    swap_blocks_mapped,
     validate_copy_host,
     validate_query_start_host,
     validate_slots_host,
@@ -40,6 +41,7 @@ __all__ = [
     "lib_path", "load_library", "multi_query_workspace", "multi_query_workspace_bytes",
     "paged_attention_decode", "paged_attention_decode_cascade", "paged_attention_multi_query",
     "paged_attention_reduce", "reshape_and_cache", "status_string", "swap_blocks",
+    "swap_blocks_mapped",
     "validate_copy_host", "validate_query_start_host", "validate_slots_host",
     "validate_tables_host", "version", "EXPORTS",
 ]

@@ -28,6 +28,7 @@ EXPORTS = {
                                             _I32, _P]),
     "pa_copy_blocks": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _I32, _I32, _I64, _I32, _P]),
     "pa_swap_blocks": (ctypes.c_int, [_P, _P, _P, _I32, _I64, _P]),
+    "pa_swap_blocks_mapped": (ctypes.c_int, [_P, _P, _P, _I32, _I64, _I64, _I64, _P]),
     "pa_validate_copy_host": (ctypes.c_int, [_P, _I32, _I64]),
     "pa_paged_attention_decode": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I32, _I32, _I32,
                                                  _I32, _I32, _I32, _I64, _F32, _I32, _I32,
@@ -347,6 +348,27 @@ def swap_blocks(src_cache, dst_cache, block_pairs, stream=None) -> None:
         pairs.ctypes.data_as(ctypes.c_void_p), pairs.shape[0], block_bytes,
         _stream_handle(stream))
     _check("pa_swap_blocks", rc)
+
+
+def swap_blocks_mapped(src_cache, dst_cache, block_pairs, stream=None) -> None:
+    """The moves of swap_blocks in one kernel: ``block_pairs`` is an int64
+    tensor [n, 2] in device or pinned host memory; either cache may be
+    pinned host memory (pageable memory is refused by the library)."""
+    import torch
+    if src_cache.shape[1:] != dst_cache.shape[1:] or src_cache.dtype != dst_cache.dtype:
+        raise ValueError("caches must share a block layout and element type")
+    if not (src_cache.is_contiguous() and dst_cache.is_contiguous()):
+        raise ValueError("caches must be contiguous")
+    if block_pairs.dtype != torch.int64 or block_pairs.dim() != 2 or block_pairs.shape[1] != 2:
+        raise ValueError("block_pairs must be an int64 tensor [n, 2]")
+    if not block_pairs.is_contiguous():
+        raise ValueError("block_pairs must be contiguous")
+    block_bytes = src_cache[0].numel() * src_cache.element_size()
+    rc = load_library().pa_swap_blocks_mapped(
+        ctypes.c_void_p(src_cache.data_ptr()), ctypes.c_void_p(dst_cache.data_ptr()),
+        ctypes.c_void_p(block_pairs.data_ptr()), block_pairs.shape[0], block_bytes,
+        src_cache.shape[0], dst_cache.shape[0], _stream_handle(stream))
+    _check("pa_swap_blocks_mapped", rc)
 
 
 def validate_copy_host(block_pairs, num_blocks: int) -> int:

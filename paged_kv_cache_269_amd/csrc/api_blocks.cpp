@@ -26,6 +26,27 @@ int elem_bytes(int32_t dtype) {
 
 bool head_dim_ok(int32_t d) { return d == 64 || d == 128; }
 
+// The address a kernel uses for `p`: device memory as is, pinned host
+// memory through its device mapping.  Pageable host memory (or anything the
+// runtime does not know) has none: nullptr.
+const void* device_view(const void* p) {
+  hipPointerAttribute_t attr{};
+  if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+    (void)hipGetLastError();  // clear the error this query leaves behind
+    return nullptr;
+  }
+  if (attr.type == hipMemoryTypeDevice) return p;
+  if (attr.type == hipMemoryTypeHost) {
+    void* dev = nullptr;  // the mapping of this very address (offsets into the allocation kept)
+    if (hipHostGetDevicePointer(&dev, const_cast<void*>(p), 0) != hipSuccess) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    return dev;
+  }
+  return nullptr;
+}
+
 }  // namespace
 
 extern "C" {
@@ -70,6 +91,25 @@ int pa_swap_blocks(const void* src_cache, void* dst_cache, const int64_t* block_
     i = j;
   }
   return PA_OK;
+}
+
+int pa_swap_blocks_mapped(const void* src_cache, void* dst_cache, const int64_t* block_pairs,
+                          int32_t num_pairs, int64_t block_bytes, int64_t src_blocks,
+                          int64_t dst_blocks, void* stream) {
+  if (num_pairs < 0 || num_pairs > kMaxGridYZ || block_bytes <= 0 || block_bytes % 16 ||
+      src_blocks <= 0 || dst_blocks <= 0)
+    return PA_ERR_SHAPE;
+  if (num_pairs == 0) return PA_OK;
+  if (!src_cache || !dst_cache || !block_pairs) return PA_ERR_NULL;
+  if ((reinterpret_cast<uintptr_t>(src_cache) | reinterpret_cast<uintptr_t>(dst_cache)) % 16)
+    return PA_ERR_UNSUPPORTED;
+  const void* src = device_view(src_cache);
+  void* dst = const_cast<void*>(device_view(dst_cache));
+  const int64_t* pairs = static_cast<const int64_t*>(device_view(block_pairs));
+  if (!src || !dst || !pairs) return PA_ERR_UNSUPPORTED;  // not reachable from the device
+  hipError_t e = pa::launch_swap_blocks(src, dst, pairs, num_pairs, block_bytes, src_blocks,
+                                        dst_blocks, (hipStream_t)stream);
+  return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
 int pa_validate_copy_host(const int32_t* block_pairs, int32_t num_pairs, int64_t num_blocks) {

@@ -85,6 +85,13 @@ hipError_t launch_reshape_and_cache(const void* key, const void* value, void* k_
 hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int num_pairs,
                               int64_t block_bytes, int64_t num_blocks, hipStream_t stream);
 
+// Blocks between two caches: pairs [num_pairs, 2] int64 (src block, dst
+// block), device-accessible; src/dst device-accessible (device memory or the
+// device mapping of pinned host memory).
+hipError_t launch_swap_blocks(const void* src, void* dst, const int64_t* pairs, int num_pairs,
+                              int64_t block_bytes, int64_t src_blocks, int64_t dst_blocks,
+                              hipStream_t stream);
+
 // Vector-ALU decode: one workgroup per (query head, sequence, partition) item.
 hipError_t launch_decode_valu(const DecodeArgs& a, int dtype, int head_dim, hipStream_t stream);
 

@@ -149,6 +149,19 @@ def test_multi_query_argument_checks_and_workspace(hiplib):
     assert _mq(lib, T=0, out=None) == OK and _mq(lib, B=0, qs=None) == OK
 
 
+def test_swap_mapped_argument_checks(hiplib):
+    """Only checks that fail before any runtime call (no GPU here)."""
+    f = hiplib.load_library().pa_swap_blocks_mapped
+    assert f(FAKE, FAKE, FAKE, -1, 4096, 8, 8, None) == SHAPE
+    assert f(FAKE, FAKE, FAKE, 70000, 4096, 8, 8, None) == SHAPE
+    assert f(FAKE, FAKE, FAKE, 2, 4100, 8, 8, None) == SHAPE      # not a multiple of 16
+    assert f(FAKE, FAKE, FAKE, 2, 4096, 0, 8, None) == SHAPE
+    assert f(None, FAKE, FAKE, 2, 4096, 8, 8, None) == NULL
+    assert f(FAKE, FAKE, None, 2, 4096, 8, 8, None) == NULL
+    assert f(FAKE, ctypes.c_void_p(0x1008), FAKE, 2, 4096, 8, 8, None) == UNSUP   # misaligned
+    assert f(None, None, None, 0, 4096, 8, 8, None) == OK
+
+
 def test_query_start_validator(hiplib):
     v = hiplib.validate_query_start_host
     assert v([0, 3, 3, 7], [5, 1, 9], 7, 4) == 0
