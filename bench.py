@@ -45,6 +45,9 @@ def parse_args(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--two-call", action="store_true",
+                    help="step = pa_reshape_and_cache then pa_paged_attention_decode (default: "
+                         "pa_reshape_and_decode, the KV write inside the decode launch)")
     ap.add_argument("--decode-only", action="store_true",
                     help="time only the decode call per step (profiling aid)")
     ap.add_argument("--pool-copies", type=int, default=2,
@@ -393,6 +396,9 @@ def main(argv=None) -> int:
         pools.append((d["k_cache"].clone(), d["v_cache"].clone()))
     out = torch.empty_like(d["q"])
     cascade = bool(w.params.get("cascade")) and part == 0
+    # one call per step (KV write inside the decode launch) unless the step
+    # is asked for as two calls, is decode only, or is the cascade form
+    fused = not (args.two_call or args.decode_only or cascade)
     if cascade:   # allocated once, outside the timed loop
         ws = pa.cascade_workspace(w.num_seqs, w.num_q_heads, w.head_dim, device=dev)
     else:
@@ -406,7 +412,12 @@ def main(argv=None) -> int:
 
     def decode(i):
         kc, vc = pools[i % len(pools)]
-        if cascade:
+        if fused:
+            pa.reshape_and_decode(out, d["q"], d["key"], d["value"], kc, vc, d["slot_mapping"],
+                                  d["block_tables"], d["context_lens"], w.scale,
+                                  w.max_context_len, partition_size=part, workspace=ws,
+                                  stream=stream)
+        elif cascade:
             pa.paged_attention_decode_cascade(out, d["q"], kc, vc, d["block_tables"],
                                               d["context_lens"], w.scale, w.max_context_len,
                                               workspace=ws, stream=stream)
@@ -425,7 +436,7 @@ def main(argv=None) -> int:
         del src, dst
 
     for i in range(args.warmup):
-        if not args.decode_only:
+        if not (args.decode_only or fused):
             reshape(i)
         decode(i)
     torch.cuda.synchronize()
@@ -437,7 +448,7 @@ def main(argv=None) -> int:
     t0 = time.perf_counter()
     for i in range(K):
         j = args.warmup + i
-        if not args.decode_only:
+        if not (args.decode_only or fused):
             reshape(j)
         ev[i][0].record(stream)
         decode(j)
@@ -451,7 +462,9 @@ def main(argv=None) -> int:
     ms_per_step = wall * 1e3 / K
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     dec_avg = float(dec_ms.mean())
-    achieved = ab["total"] / (dec_avg * 1e-3) / 1e9
+    # the timed launch: decode alone, or decode with the KV write inside it
+    launch_bytes = ab["total"] + (W.reshape_bytes(w) if fused else 0)
+    achieved = launch_bytes / (dec_avg * 1e-3) / 1e9
     traffic = stored_traffic(args.config)
 
     result = {
@@ -474,9 +487,12 @@ def main(argv=None) -> int:
                    "context_len_mean": float(w.context_lens.mean()),
                    "context_len_max": int(w.max_context_len), "num_blocks": w.num_blocks,
                    "pool_copies": len(pools),
-                   "entry": ("pa_paged_attention_decode_cascade" if cascade
+                   "entry": ("pa_reshape_and_decode" if fused else
+                             "pa_paged_attention_decode_cascade" if cascade
                              else "pa_paged_attention_decode"),
-                   "step": ("decode" if args.decode_only else "reshape_and_cache + decode")
+                   "step": ("decode" if args.decode_only else
+                            "KV write + decode in one call" if fused else
+                            "reshape_and_cache + decode")
                            + (" + split-K reduce" if part and w.max_context_len > part else "")},
         "seqs_per_s": round(w.num_seqs / (ms_per_step * 1e-3), 1),
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
@@ -487,13 +503,14 @@ def main(argv=None) -> int:
                      "traffic": traffic,
                      "kernel": ("pa_paged_attention_decode_cascade (shared-prefix kernel + "
                                 "decode kernel)" if cascade else
-                                "pa_paged_attention_decode (decode kernel"
+                                ("pa_reshape_and_decode (decode kernel with the KV write"
+                                 if fused else "pa_paged_attention_decode (decode kernel")
                                 + (" + split-K reduce" if part and w.max_context_len > part
                                    else "") + ")"),
                      "launch_us_avg": round(dec_avg * 1e3, 2),
                      "launch_us_p10": round(float(np.percentile(dec_ms, 10)) * 1e3, 2),
                      "launch_us_p90": round(float(np.percentile(dec_ms, 90)) * 1e3, 2),
-                     "algorithmic_bytes_per_launch": ab["total"]},
+                     "algorithmic_bytes_per_launch": launch_bytes},
     }
     if args.query_len > 0:
         result["multi_query"] = multi_query_bench(args, w, d, pools, part, stream)

@@ -126,6 +126,39 @@ int pa_paged_attention_decode(void* out, const void* q, const void* k_cache,
                               void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * One decode step in one call: the KV write of each sequence's new token
+ * followed by decode attention ([CX] §1.1: the new token's K and V join the
+ * cache, then o_t attends over K_{1:t}, V_{1:t} with token t included).
+ * The result equals
+ *     pa_reshape_and_cache(key, value, k_cache, v_cache, slot_mapping,
+ *                          num_seqs, ...);
+ *     pa_paged_attention_decode(out, q, k_cache, v_cache, ...);
+ * with one new token per sequence: key, value [num_seqs, num_kv_heads,
+ * head_dim] (row s = sequence s's token), slot_mapping [num_seqs] int64
+ * (negative or >= block_size * num_blocks: not written).  Every other
+ * argument, the workspace rule and the errors are those of
+ * pa_paged_attention_decode; key, value and slot_mapping must not be NULL
+ * when num_seqs > 0.
+ *
+ * Precondition (the normal decode step, where slot_mapping[s] is the slot of
+ * position context_lens[s] - 1 of sequence s's table): no context reads, in
+ * this call, a slot written in this call other than its own last position.
+ * The decode kernels then store each new row once and use it from registers
+ * where a context ends with it, so no kernel waits for the write; when the
+ * precondition does not hold the result is undefined.  The streaming kernel
+ * (16-token blocks, >= 8 partitions, <= 64 sequences, grouped heads) is
+ * preceded by the KV-write kernel instead.
+ */
+int pa_reshape_and_decode(void* out, const void* q, const void* key, const void* value,
+                          void* k_cache, void* v_cache, const int64_t* slot_mapping,
+                          const int32_t* block_tables, const int32_t* context_lens,
+                          int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                          int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                          int64_t num_blocks, float scale, int32_t dtype, int32_t partition_size,
+                          int32_t max_context_len, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+/*
  * Split-K merge.  Sequence s has P = ceil(L / partition_size) partitions,
  * L = context_lens[s] clamped to [0, partition_size * max_partitions].  For
  * query head h the partials are

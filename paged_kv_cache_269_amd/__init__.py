@@ -24,6 +24,7 @@ from ._binding import (  # noqa: F401
     paged_attention_multi_query,
     paged_attention_reduce,
     reshape_and_cache,
+    reshape_and_decode,
     status_string,
     swap_blocks,
     swap_blocks_mapped,

@@ -83,7 +83,9 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
                 int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                 int32_t max_blocks_per_seq, int64_t num_blocks, float scale, int32_t dtype,
                 int32_t partition_size, int32_t max_context_len, void* workspace,
-                size_t workspace_bytes, void* stream, bool cascade);
+                size_t workspace_bytes, void* stream, bool cascade,
+                const void* new_k = nullptr, const void* new_v = nullptr,
+                const int64_t* new_slots = nullptr);
 
 }  // namespace
 
@@ -94,7 +96,8 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
                 int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                 int32_t max_blocks_per_seq, int64_t num_blocks, float scale, int32_t dtype,
                 int32_t partition_size, int32_t max_context_len, void* workspace,
-                size_t workspace_bytes, void* stream, bool cascade) {
+                size_t workspace_bytes, void* stream, bool cascade,
+                const void* new_k, const void* new_v, const int64_t* new_slots) {
   if (!elem_bytes(dtype) || !block_size_ok(block_size) || !head_dim_ok(head_dim))
     return PA_ERR_UNSUPPORTED;
   if (partition_size < 0 || partition_size % kBlock) return PA_ERR_UNSUPPORTED;
@@ -145,6 +148,7 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   a.max_partitions = (int)parts;
   a.scale_log2 = scale * 1.4426950408889634f;
   a.block_size = block_size;
+  a.num_blocks = num_blocks;
 
   const hipStream_t st = (hipStream_t)stream;
   const int group = num_q_heads / num_kv_heads;
@@ -164,6 +168,21 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
     a.prefix_l = po.l;
     a.prefix_o = po.o;
     if (pa::launch_prefix(a, po, dtype, head_dim, st) != hipSuccess) return PA_ERR_LAUNCH;
+  }
+  if (new_slots != nullptr) {
+    // New tokens' K/V: written by the decode kernel itself, except on the
+    // streaming kernel, which is preceded by the KV-write kernel.
+    if (use_mfma && pa::decode_mfma_streams(a)) {
+      if (pa::launch_reshape_and_cache(new_k, new_v, const_cast<void*>(k_cache),
+                                       const_cast<void*>(v_cache), new_slots, num_seqs,
+                                       num_kv_heads, head_dim, elem_bytes(dtype), block_size,
+                                       num_blocks, st) != hipSuccess)
+        return PA_ERR_LAUNCH;
+    } else {
+      a.new_k = new_k;
+      a.new_v = new_v;
+      a.new_slots = new_slots;
+    }
   }
   hipError_t e = use_mfma ? pa::launch_decode_mfma(a, dtype, head_dim, st)
                           : pa::launch_decode_valu(a, dtype, head_dim, st);
@@ -242,6 +261,21 @@ int pa_paged_attention_decode(void* out, const void* q, const void* k_cache, con
                      num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks, scale,
                      dtype, partition_size, max_context_len, workspace, workspace_bytes, stream,
                      false);
+}
+
+int pa_reshape_and_decode(void* out, const void* q, const void* key, const void* value,
+                          void* k_cache, void* v_cache, const int64_t* slot_mapping,
+                          const int32_t* block_tables, const int32_t* context_lens,
+                          int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                          int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                          int64_t num_blocks, float scale, int32_t dtype, int32_t partition_size,
+                          int32_t max_context_len, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  if (num_seqs > 0 && (!key || !value || !slot_mapping)) return PA_ERR_NULL;
+  return decode_impl(out, q, k_cache, v_cache, block_tables, context_lens, num_seqs, num_q_heads,
+                     num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks, scale,
+                     dtype, partition_size, max_context_len, workspace, workspace_bytes, stream,
+                     false, key, value, slot_mapping);
 }
 
 size_t pa_cascade_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim) {

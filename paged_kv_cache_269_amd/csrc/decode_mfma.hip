@@ -109,16 +109,37 @@ __device__ __forceinline__ void mfma_item(const DecodeArgs& a, const int unit, c
   const HeadTile t = head_tile(a, unit, s);
   const int nblocks = (L + kBlockSize - 1) / kBlockSize;
   const int nparts = (nblocks + a.part_blocks - 1) / a.part_blocks;
+  const int32_t* __restrict__ bt = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
+
+  // Fused KV write: the first head tile of each KV head, in the partition
+  // holding the context's end, stores the new token's row; every item takes
+  // the row from registers where its context ends with that slot.  K: this
+  // lane's chunk of the row in the load layout (chunk lane % CPR); V: its
+  // slice n in the P.V operand layout.
+  constexpr int RB = D * 2;  // bytes of one K or V row
+  const int hchunks = (a.num_q_heads / a.num_kv_heads + 15) >> 4;
+  const NewToken nt = new_token<BS>(a, bt, s, t.kvh, L,
+                                    unit % hchunks == 0 && part == max(nparts, 1) - 1, RB);
+  const int lane = ln.n + 16 * ln.g;
+  const u32x4 nkc = buf_load16(new_row_rsrc(a, a.new_k, s, t.kvh, RB), (lane % S::CPR) * 16);
+  const VT nvc = S::VS::template load<false>(new_row_rsrc(a, a.new_v, s, t.kvh, RB),
+                                             EPL * ln.n * 2);
+  auto store_new = [&]() {
+    if (nt.store && (WAVE_ITEM || w == 0)) {
+      if (lane < S::CPR) store_row_part(a.k_cache, nt.off + lane * 16, nkc);
+      if (ln.g == 0) store_row_part(a.v_cache, nt.off + EPL * ln.n * 2, nvc);
+    }
+  };
+
   if (L == 0) {
     const int t0 = WAVE_ITEM ? (int)(threadIdx.x & 63) : (int)threadIdx.x;
     const int tn = WAVE_ITEM ? 64 : NW * 64;
     for (int i = t0; i < t.nh * D; i += tn) store_elem<DT>(a.out, t.orow0 * D + i, 0.f);
+    store_new();
     return;
   }
   u32x4 qb[S::NJ];
   load_q<DT, D>(a, t, ln, qb);
-
-  const int32_t* __restrict__ bt = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
   // Shared-prefix launches (one pass): the leading `pre` blocks were done by
   // the prefix kernel; their state joins the merge below.
   const int pre = (!WAVE_ITEM && a.prefix_blocks != nullptr) ? a.prefix_blocks[s] : 0;
@@ -138,11 +159,24 @@ __device__ __forceinline__ void mfma_item(const DecodeArgs& a, const int unit, c
   // Descriptors of the wave's kk-th tile and the number of its tokens in the
   // context; empty past the wave's last tile, and tokens in a block outside
   // the pool do not count.
-  auto tile = [&](int kk, const TileIds<BS>& ids, int& limit) {
+  auto tile = [&](int kk, const TileIds<BS>& ids, int& limit, int& tj) {
     const int j = j0 + min(kk, nk - 1) * STRIDE;
     const bool ok = kk < nk;
     limit = ok ? tile_limit<BS>(a, ids, L - j * kBlockSize) : 0;
+    tj = ok ? j : -1;
     return tile_desc<BS, S::TILE_BYTES>(a, ids, j, t.kvh, ok);
+  };
+  // The context's last token is the new one: its K row (load jj, lane l =
+  // row (64 jj + l) / CPR) and V row (slice e = row g + 4e) come from registers.
+  auto substitute = [&](u32x4 (&kr)[S::NJ], VT (&vr)[4], int tj) {
+    if (nt.sub && tj == nt.tile) {
+#pragma unroll
+      for (int jj = 0; jj < S::NJ; ++jj)
+        if ((jj * 64 + lane) / S::CPR == nt.row) kr[jj] = nkc;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (ln.g + 4 * e == nt.row) vr[e] = nvc;
+    }
   };
 
   // Software pipeline over the wave's blocks: DEPTH register sets; while
@@ -153,12 +187,12 @@ __device__ __forceinline__ void mfma_item(const DecodeArgs& a, const int unit, c
   // past-the-end step consumes nothing.
   u32x4 kr[DEPTH][S::NJ];
   VT vr[DEPTH][4];
-  int lim[DEPTH];
+  int lim[DEPTH], tjs[DEPTH];
   auto pipeline = [&](auto shared) {
     constexpr bool SH = decltype(shared)::value;
     static_for<0, DEPTH - 1>([&](auto dc) {
       constexpr int d = decltype(dc)::value;
-      load_tile<DT, D, SH>(tile(d, id_at(d), lim[d]), ln, kr[d], vr[d]);
+      load_tile<DT, D, SH>(tile(d, id_at(d), lim[d], tjs[d]), ln, kr[d], vr[d]);
     });
     TileIds<BS> next_id = id_at(DEPTH - 1);
     for (int k = 0; k < nk; k += DEPTH) {
@@ -168,7 +202,8 @@ __device__ __forceinline__ void mfma_item(const DecodeArgs& a, const int unit, c
         const int kn = k + d + DEPTH - 1;  // tile whose loads are issued now
         const TileIds<BS> id = next_id;
         next_id = id_at(kn + 1);
-        load_tile<DT, D, SH>(tile(kn, id, lim[dn]), ln, kr[dn], vr[dn]);
+        load_tile<DT, D, SH>(tile(kn, id, lim[dn], tjs[dn]), ln, kr[dn], vr[dn]);
+        substitute(kr[d], vr[d], tjs[d]);
         consume_any<DT, D>(st, qb, kr[d], vr[d], lim[d], a.scale_log2, ln, kst);
       });
     }
@@ -186,6 +221,7 @@ __device__ __forceinline__ void mfma_item(const DecodeArgs& a, const int unit, c
     else
       pipeline(std::false_type{});
   }
+  store_new();
 
   if constexpr (WAVE_ITEM) {
     write_wave_item<DT, D>(a, st, t, part, nparts, ln);
@@ -564,8 +600,10 @@ hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
   const int group = a.num_q_heads / a.num_kv_heads;
   const int64_t items = (int64_t)a.num_kv_heads * ((group + 15) / 16) * a.num_seqs *
                         a.max_partitions;
-  if (a.max_partitions >= kWaveItemParts && a.num_seqs <= kStreamMaxSeqs && items < INT32_MAX)
+  if (decode_mfma_streams(a)) {
+    if (a.new_slots != nullptr) return hipErrorInvalidValue;  // the streaming kernel does no KV write
     return launch_stream_shape<DT, D, PA_MFMA_STREAM_WAVES, PA_MFMA_STREAM_DEPTH>(a, items, stream);
+  }
   if (a.max_partitions >= kWaveItemParts)
     return launch_wave_shape<DT, D, PA_MFMA_WAVE_ITEM_WAVES, PA_MFMA_WAVE_ITEM_DEPTH>(a, stream);
   return a.part_blocks >= kLongItemBlocks
@@ -574,6 +612,14 @@ hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
 }
 
 }  // namespace
+
+bool decode_mfma_streams(const DecodeArgs& a) {
+  if (a.block_size != kBlockSize) return false;
+  const int group = a.num_q_heads / a.num_kv_heads;
+  const int64_t items = (int64_t)a.num_kv_heads * ((group + 15) / 16) * a.num_seqs *
+                        a.max_partitions;
+  return a.max_partitions >= kWaveItemParts && a.num_seqs <= kStreamMaxSeqs && items < INT32_MAX;
+}
 
 hipError_t launch_decode_mfma(const DecodeArgs& a, int dtype, int head_dim, hipStream_t stream) {
   switch (dtype * 1000 + head_dim) {

@@ -72,14 +72,32 @@ __device__ __forceinline__ void valu_item(const DecodeArgs& a, const int h, cons
   const int nblocks = (L + kBlockSize - 1) / kBlockSize;
   const int nparts = (nblocks + a.part_blocks - 1) / a.part_blocks;
   const int64_t orow = (int64_t)s * a.num_q_heads + h;
+  const int32_t* __restrict__ bt = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
+
+  // Fused KV write: the first query head of each KV head, in the partition
+  // holding the context's end, stores the new token's row (lanes of row 0,
+  // chunk c each); every item takes the row from registers where its context
+  // ends with that slot.
+  constexpr int RB = D * Elem<DT>::bytes;  // bytes of one K or V row
+  const NewToken nt = new_token<BS>(a, bt, s, kvh, L, h % group == 0 && part == max(nparts, 1) - 1,
+                                    RB);
+  const u32x4 nkc = buf_load16(new_row_rsrc(a, a.new_k, s, kvh, RB), c * 16);
+  const u32x4 nvc = buf_load16(new_row_rsrc(a, a.new_v, s, kvh, RB), c * 16);
+  auto store_new = [&]() {
+    if (nt.store && (WAVE_ITEM || w == 0) && row == 0) {
+      store_row_part(a.k_cache, nt.off + c * 16, nkc);
+      store_row_part(a.v_cache, nt.off + c * 16, nvc);
+    }
+  };
+
   if (L == 0) {
     const int t0 = WAVE_ITEM ? lane : (int)threadIdx.x, tn = WAVE_ITEM ? 64 : NW * 64;
     for (int d = t0; d < D; d += tn) store_elem<DT>(a.out, orow * D + d, 0.f);
+    store_new();
     return;
   }
 
   const u32x4 qv = reinterpret_cast<const u32x4*>(a.q)[orow * (D / VEC) + c];
-  const int32_t* __restrict__ bt = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
   // Shared-prefix launches (one pass): the leading `pre` blocks were done by
   // the prefix kernel; their state joins the merge below.
   const int pre = (!WAVE_ITEM && a.prefix_blocks != nullptr) ? a.prefix_blocks[s] : 0;
@@ -102,10 +120,11 @@ __device__ __forceinline__ void valu_item(const DecodeArgs& a, const int h, cons
   // Descriptors of the wave's kk-th tile and the number of its tokens in the
   // context; past the wave's last tile the descriptors are empty and no
   // token counts, nor do tokens in a block whose id lies outside the pool.
-  auto tile = [&](int kk, const TileIds<BS>& ids, int& limit) {
+  auto tile = [&](int kk, const TileIds<BS>& ids, int& limit, int& tj) {
     const int j = j0 + min(kk, nk - 1) * STRIDE;
     const bool ok = kk < nk;
     limit = ok ? tile_limit<BS>(a, ids, L - j * kBlockSize) : 0;
+    tj = ok ? j : -1;
     return tile_desc<BS, S::TILE_BYTES>(a, ids, j, kvh, ok);
   };
   // Load i covers the tile's i-th KiB (TPL whole rows); which block part it
@@ -155,7 +174,16 @@ __device__ __forceinline__ void valu_item(const DecodeArgs& a, const int h, cons
     }
     m = mn;
   };
-  auto consume_block = [&](const u32x4 (&kr)[NLD], const u32x4 (&vr)[NLD], int limit) {
+  auto consume_block = [&](u32x4 (&kr)[NLD], u32x4 (&vr)[NLD], int limit, int tj) {
+    if (nt.sub && tj == nt.tile) {  // the context's last token is the new one
+#pragma unroll
+      for (int i = 0; i < NLD; ++i) {
+        if (i * TPL + row == nt.row) {
+          kr[i] = nkc;
+          vr[i] = nvc;
+        }
+      }
+    }
     if (limit == kBlockSize)
       consume(std::false_type{}, kr, vr, limit);
     else
@@ -169,11 +197,11 @@ __device__ __forceinline__ void valu_item(const DecodeArgs& a, const int h, cons
   // are the same on every path -- no branch around a load -- and a
   // past-the-end step consumes nothing.
   u32x4 kr[DEPTH][NLD], vr[DEPTH][NLD];
-  int lim[DEPTH];
+  int lim[DEPTH], tjs[DEPTH];
   auto pipeline = [&](auto shared) {
     static_for<0, DEPTH - 1>([&](auto dc) {
       constexpr int d = decltype(dc)::value;
-      load(shared, tile(d, id_at(d), lim[d]), kr[d], vr[d]);
+      load(shared, tile(d, id_at(d), lim[d], tjs[d]), kr[d], vr[d]);
     });
     TileIds<BS> next_id = id_at(DEPTH - 1);
     for (int k = 0; k < nk; k += DEPTH) {
@@ -183,8 +211,8 @@ __device__ __forceinline__ void valu_item(const DecodeArgs& a, const int h, cons
         const int kn = k + d + DEPTH - 1;  // tile whose loads are issued now
         const TileIds<BS> id = next_id;
         next_id = id_at(kn + 1);
-        load(shared, tile(kn, id, lim[dn]), kr[dn], vr[dn]);
-        consume_block(kr[d], vr[d], lim[d]);
+        load(shared, tile(kn, id, lim[dn], tjs[dn]), kr[dn], vr[dn]);
+        consume_block(kr[d], vr[d], lim[d], tjs[d]);
       });
     }
   };
@@ -201,6 +229,7 @@ __device__ __forceinline__ void valu_item(const DecodeArgs& a, const int h, cons
     else
       pipeline(std::false_type{});
   }
+  store_new();
 
   if constexpr (WAVE_ITEM) {
     // Merge this wave's TPL row states in registers; row 0 writes.

@@ -93,6 +93,55 @@ __device__ __forceinline__ int tile_limit(const DecodeArgs& a, const TileIds<BS>
   return n;
 }
 
+// Fused KV write: where sequence s's new token goes (slot_mapping[s], the
+// rule of [CX] §2.2: block * block_size + offset) and whether it is the last
+// position of the context -- then the item holding tile (L-1)/16 uses the
+// new row itself, as if the write had come first ([CX] §1.1: o_t attends to
+// K_{1:t}, token t included).  `owner`: this item is the one of its
+// (sequence, KV head) that stores the row.
+struct NewToken {
+  bool store;     // store the row (owner, slot inside the pool)
+  bool sub;       // tile `tile`, row `row` of the context take the new row
+  int tile, row;
+  int64_t off;    // byte offset of the slot's row of KV head kvh in either cache
+};
+
+template <int BS>
+__device__ __forceinline__ NewToken new_token(const DecodeArgs& a, const int32_t* bt, int s,
+                                              int kvh, int L, bool owner, int row_bytes) {
+  NewToken t{false, false, 0, 0, 0};
+  if (a.new_slots == nullptr) return t;
+  const int64_t slot = a.new_slots[s];
+  if (slot < 0 || slot >= a.num_blocks * BS) return t;
+  t.store = owner;
+  t.off = ((slot / BS) * a.num_kv_heads + kvh) * (int64_t)(BS * row_bytes) +
+          (slot % BS) * (int64_t)row_bytes;
+  if (L > 0) {
+    const int64_t pos = (int64_t)bt[(L - 1) / BS] * BS + (L - 1) % BS;
+    t.sub = pos == slot;
+    t.tile = (L - 1) / kBlockSize;
+    t.row = (L - 1) % kBlockSize;
+  }
+  return t;
+}
+
+// This lane's 16-byte chunk `c` of sequence s's new row for KV head kvh
+// (zeros when there is no fused write: the descriptor is then empty).
+__device__ __forceinline__ Rsrc new_row_rsrc(const DecodeArgs& a, const void* base, int s,
+                                             int kvh, int row_bytes) {
+  const bool on = a.new_slots != nullptr;
+  const char* p = on ? static_cast<const char*>(base) +
+                           ((int64_t)s * a.num_kv_heads + kvh) * row_bytes
+                     : static_cast<const char*>(a.q);
+  return make_rsrc(p, on ? row_bytes : 0);
+}
+
+// Store `n` bytes (8 or 16) of a new row at byte `off` of a cache.
+template <typename T>
+__device__ __forceinline__ void store_row_part(const void* cache, int64_t off, const T& v) {
+  *reinterpret_cast<T*>(static_cast<char*>(const_cast<void*>(cache)) + off) = v;
+}
+
 // Sequence that grid slot `slot` works on.  The hardware dispatcher starts
 // workgroups in grid order, so slots take the sequences in decreasing order
 // of context length (ties by index): the longest items start first and the

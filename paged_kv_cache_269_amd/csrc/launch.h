@@ -35,6 +35,15 @@ struct DecodeArgs {
   const float* prefix_m;         // [B, Hq] max score, base 2
   const float* prefix_l;         // [B, Hq] sum of exp2(score - max)
   const float* prefix_o;         // [B, Hq, D] normalised output of the prefix part
+  // Fused KV write (new_slots != nullptr): each sequence's new token, rows
+  // new_k / new_v [B, Hkv, D], goes to slot new_slots[s] of the caches (skipped
+  // when the slot is negative or past the pool).  One item per (sequence, KV
+  // head) stores it; every item whose context ends with that slot takes the
+  // row from new_k / new_v instead of reading the cache.
+  const void* new_k;
+  const void* new_v;
+  const int64_t* new_slots;     // [B]
+  int64_t num_blocks;           // N (slot bound of the write)
 };
 
 // Outputs of the shared-prefix kernel (the same arrays DecodeArgs reads).
@@ -98,6 +107,10 @@ hipError_t launch_decode_valu(const DecodeArgs& a, int dtype, int head_dim, hipS
 // Matrix-core decode for grouped heads: one workgroup per (kv head x 16-head
 // tile, sequence, partition) item.
 hipError_t launch_decode_mfma(const DecodeArgs& a, int dtype, int head_dim, hipStream_t stream);
+
+// Whether launch_decode_mfma takes the streaming kernel for these arguments
+// (it does no fused KV write: the caller writes first).
+bool decode_mfma_streams(const DecodeArgs& a);
 
 // Shared-prefix pass: for runs of consecutive sequences whose block tables
 // start with the same full blocks, the attention over those blocks, once per

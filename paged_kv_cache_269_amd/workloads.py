@@ -148,8 +148,8 @@ def _normal_pool(ss: np.random.SeedSequence, shape, dtype: str,
 def _nan_fill(a: np.ndarray, dtype: str, index) -> None:
     if dtype == "f32":
         a[index] = np.nan
-    else:
-        a[index] = _NAN_BITS[dtype]
+    else:  # a quiet-NaN bit pattern (f16 pools are float16, bf16 pools uint16 bits)
+        a.view(np.uint16)[index] = _NAN_BITS[dtype]
 
 
 def _draw_lengths(rng: np.random.Generator, p: dict) -> np.ndarray:

@@ -75,6 +75,34 @@ def test_decode_argument_checks(hiplib):
     assert _decode(lib, B=0, out=None) == OK
 
 
+def _fused(lib, **kw):
+    a = dict(out=FAKE, q=FAKE, key=FAKE, value=FAKE, k=FAKE, v=FAKE, slots=FAKE, bt=FAKE,
+             cl=FAKE, B=2, Hq=8, Hkv=2, D=128, bs=16, M=4, N=10, scale=0.1, dtype=1, part=512,
+             maxlen=64, ws=None, wsb=0, stream=None)
+    a.update(kw)
+    return lib.pa_reshape_and_decode(a["out"], a["q"], a["key"], a["value"], a["k"], a["v"],
+                                     a["slots"], a["bt"], a["cl"], a["B"], a["Hq"], a["Hkv"],
+                                     a["D"], a["bs"], a["M"], a["N"], a["scale"], a["dtype"],
+                                     a["part"], a["maxlen"], a["ws"], a["wsb"], a["stream"])
+
+
+def test_fused_write_decode_argument_checks(hiplib):
+    """pa_reshape_and_decode: the decode checks, plus the new tokens' rows
+    and slots; all refused before any launch."""
+    lib = hiplib.load_library()
+    assert _fused(lib, key=None) == NULL
+    assert _fused(lib, value=None) == NULL
+    assert _fused(lib, slots=None) == NULL
+    assert _fused(lib, out=None) == NULL
+    assert _fused(lib, D=96) == UNSUP
+    assert _fused(lib, bs=24) == UNSUP
+    assert _fused(lib, part=100) == UNSUP
+    assert _fused(lib, Hq=6, Hkv=4) == SHAPE
+    assert _fused(lib, N=0) == SHAPE
+    assert _fused(lib, maxlen=1024, M=64) == WS
+    assert _fused(lib, B=0, key=None, slots=None) == OK
+
+
 def test_workspace_bytes(hiplib):
     lib = hiplib.load_library()
     f = lib.pa_decode_workspace_bytes

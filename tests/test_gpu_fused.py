@@ -1,0 +1,192 @@
+"""GPU parity of pa_reshape_and_decode: the KV write of each sequence's new
+token inside the decode launch.
+
+Every case starts from a pool whose new-token slots hold NaN (the
+generator's poison), so a kernel that read its context's last token from the
+cache instead of taking the new row would produce NaN.  Checked: the pool after
+the call byte-identical to the oracle's KV write; the output within the
+element type's tolerance of the float64 oracle and bit-identical to the
+two-call form (pa_reshape_and_cache, then pa_paged_attention_decode) on a fresh
+copy of the same inputs; one-token contexts return the new V row exactly.
+"""
+import copy
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from paged_kv_cache_269_amd import workloads as W
+
+from parity import Run, check_close, oracle_rows, tensor_to_np, to_f64
+
+pytestmark = pytest.mark.gpu
+
+SMALL = {
+    "tiny": {},
+    "llama7b": dict(num_seqs=6, len_lo=1, len_hi=1300),
+    "gqa": dict(num_seqs=10, len_median=700, len_cap=2100),
+    "shared_prefix": dict(num_seqs=9),
+    "long_context": dict(num_seqs=3, len_lo=3000, len_hi=7000),
+}
+
+
+def announce(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def fused(run, part, slots=None, key=None, value=None):
+    w, d = run.w, run.dev
+    out = torch.empty_like(d["q"])
+    run.pa.reshape_and_decode(out, d["q"], d["key"] if key is None else key,
+                              d["value"] if value is None else value, d["k_cache"], d["v_cache"],
+                              d["slot_mapping"] if slots is None else slots, d["block_tables"],
+                              d["context_lens"], w.scale, w.max_context_len, partition_size=part)
+    torch.cuda.synchronize()
+    return out
+
+
+def two_calls(w, cuda, part):
+    run = Run(w, cuda)
+    run.reshape()
+    return run.decode(partition_size=part)
+
+
+def pool_bits(run, w):
+    view = np.uint32 if w.dtype == "f32" else np.uint16
+    return (tensor_to_np(run.dev["k_cache"], w.dtype).view(view),
+            tensor_to_np(run.dev["v_cache"], w.dtype).view(view))
+
+
+def full_oracle(w):
+    B, Hq = w.num_seqs, w.num_q_heads
+    return oracle_rows(w, np.repeat(np.arange(B), Hq), np.tile(np.arange(Hq), B)).reshape(
+        B, Hq, w.head_dim)
+
+
+def after_write(w):
+    """The workload with the oracle's KV write applied to copies of its pools
+    (``w`` itself keeps the NaN-poisoned slots for the next upload)."""
+    w2 = copy.copy(w)
+    w2.k_cache, w2.v_cache = w.k_cache.copy(), w.v_cache.copy()
+    oracle.reshape_and_cache(w2.key, w2.value, w2.k_cache, w2.v_cache, w2.slot_mapping, w2.dtype)
+    return w2
+
+
+def check_case(w, cuda, parts, label):
+    """Fused call on fresh inputs for each partition size: pool, oracle,
+    two-call form."""
+    w2 = after_write(w)
+    ref = full_oracle(w2)
+    view = np.uint32 if w.dtype == "f32" else np.uint16
+    for part in parts:
+        run = Run(w, cuda)
+        out = fused(run, part)
+        kc, vc = pool_bits(run, w)
+        assert np.array_equal(kc, w2.k_cache.view(view)), f"{label}: k_cache differs"
+        assert np.array_equal(vc, w2.v_cache.view(view)), f"{label}: v_cache differs"
+        got_raw = tensor_to_np(out, w.dtype)
+        stats = check_close(to_f64(got_raw, w.dtype), ref, w.dtype, f"{label} partition {part}")
+        base = tensor_to_np(two_calls(w, cuda, part), w.dtype)
+        assert np.array_equal(got_raw.view(view), base.view(view)), \
+            f"{label} partition {part}: differs from the two-call form"
+        G = w.num_q_heads // w.num_kv_heads
+        for s in np.nonzero(w.context_lens == 1)[0]:
+            for h in range(w.num_q_heads):
+                assert np.array_equal(got_raw[s, h], w.value[s, h // G]), "L=1 not exact"
+        announce(label, "partition", part, stats)
+
+
+@pytest.mark.parametrize("name", W.CONFIG_ORDER)
+def test_fused_small_configs(cuda, name):
+    announce("fused small", name)
+    w = W.generate(name, **SMALL[name])
+    check_case(w, cuda, sorted({w.partition_size, 0, 16, 512}), name)
+
+
+EDGE_LENS = [1, 15, 16, 17, 511, 512, 513, 1024, 1025, 0, 2000]
+
+
+@pytest.mark.parametrize("dtype,D,G", [
+    ("f32", 64, 1), ("f32", 128, 4), ("f16", 128, 1), ("f16", 64, 2), ("bf16", 64, 8),
+    ("bf16", 128, 8), ("bf16", 128, 3), ("bf16", 128, 32),
+])
+def test_fused_edge_lengths(cuda, dtype, D, G):
+    announce("fused edge", dtype, D, G)
+    w = W.generate("long_context", dtype=dtype, head_dim=D, num_kv_heads=2, num_q_heads=2 * G,
+                   lens=EDGE_LENS, seed=78)
+    check_case(w, cuda, (0, 16, 256, 2048), f"edge {dtype} D{D} G{G}")
+
+
+@pytest.mark.parametrize("bs", [8, 32])
+@pytest.mark.parametrize("dtype,G", [("f16", 1), ("bf16", 4), ("f32", 1)])
+def test_fused_block_sizes(cuda, bs, dtype, G):
+    announce("fused block size", bs, dtype, G)
+    w = W.generate("long_context", dtype=dtype, head_dim=128, num_kv_heads=2,
+                   num_q_heads=2 * G, lens=EDGE_LENS, seed=79, block_size=bs)
+    check_case(w, cuda, (0, 16, 512), f"bs{bs} {dtype} G{G}")
+
+
+@pytest.mark.parametrize("name", ["llama7b", "gqa"])
+def test_fused_full_size(cuda, name):
+    """The full workload in the benchmark's launch configuration: pool after
+    the call equal to the two-call form's, output bit-identical to it, and
+    sampled rows against the oracle."""
+    announce("fused full", name)
+    w = W.generate(name)
+    run = Run(w, cuda)
+    out = fused(run, w.partition_size if name != "llama7b" else 0)
+    base_run = Run(w, cuda)
+    base_run.reshape()
+    base = base_run.decode(partition_size=w.partition_size if name != "llama7b" else 0)
+    view = np.uint32 if w.dtype == "f32" else np.uint16
+    assert np.array_equal(tensor_to_np(out, w.dtype).view(view),
+                          tensor_to_np(base, w.dtype).view(view))
+    for a, b in zip(pool_bits(run, w), pool_bits(base_run, w)):
+        assert np.array_equal(a, b)
+    w2 = after_write(w)
+    rng = np.random.default_rng(5)
+    B, Hq = w.num_seqs, w.num_q_heads
+    flat = rng.choice(B * Hq, size=48, replace=False)
+    seqs, heads = flat // Hq, flat % Hq
+    ref = oracle_rows(w2, seqs, heads)
+    got = to_f64(tensor_to_np(out, w.dtype)[seqs, heads], w.dtype)
+    announce(name, check_close(got, ref, w.dtype, f"{name} fused full size"))
+
+
+def test_fused_slots_elsewhere(cuda):
+    """Slots that are not a context's last position: the rows land there, no
+    context reads them, and the output is plain decode of the cache as it
+    was (padding slots write nothing)."""
+    w = W.generate("llama7b", num_seqs=5, len_lo=3, len_hi=300, seed=11)
+    run = Run(w, cuda)
+    run.reshape()  # the newest positions now hold the new rows
+    base = run.decode(partition_size=0)
+    bs, B = w.block_size, w.num_seqs
+    used = set()
+    for s in range(B):
+        used.update(int(b) for b in w.block_tables[s, :(int(w.context_lens[s]) + bs - 1) // bs])
+    used.update(int(b) for b in w.block_tables.ravel())  # table padding too
+    free = [b for b in range(w.num_blocks) if b not in used]
+    assert len(free) >= B
+    slots = np.array([free[s] * bs + (3 * s) % bs for s in range(B)], np.int64)
+    slots[1] = -1  # padding: no write
+    dev = cuda
+    gen = np.random.default_rng(12)
+    key = (gen.standard_normal(w.key.shape).astype(np.float32)).astype(np.float16)
+    value = (gen.standard_normal(w.value.shape).astype(np.float32)).astype(np.float16)
+    out = fused(run, 0, slots=torch.from_numpy(slots).to(dev), key=torch.from_numpy(key).to(dev),
+                value=torch.from_numpy(value).to(dev))
+    assert np.array_equal(tensor_to_np(out, w.dtype).view(np.uint16),
+                          tensor_to_np(base, w.dtype).view(np.uint16))
+    kc, vc = pool_bits(run, w)
+    for s in range(B):
+        if slots[s] < 0:
+            continue
+        blk, off = divmod(int(slots[s]), bs)
+        assert np.array_equal(kc[blk, :, off], key[s].view(np.uint16))
+        assert np.array_equal(vc[blk, :, off], value[s].view(np.uint16))
+    # the padded sequence's free block is untouched (still the generator's NaN)
+    assert np.isnan(tensor_to_np(run.dev["k_cache"], w.dtype)[free[1]].astype(np.float32)).all()
