@@ -74,21 +74,22 @@ def kernel_source_hash() -> str:
     still describe the code being run."""
     h = hashlib.sha256()
     for f in ("common.h", "items.h", "launch.h", "mfma_tile.h", "decode_valu.hip",
-              "decode_mfma.hip", "prefix.hip", "reduce.hip", "api.cpp"):
+              "decode_mfma.hip", "prefix.hip", "reduce.hip", "reshape_and_cache.hip", "api.cpp"):
         with open(os.path.join(ROOT, "paged_kv_cache_269_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
 def stored_traffic(config: str):
-    """HBM bytes per decode launch from the committed rocprofv3 counter summary,
-    if it was taken on the current kernel sources and this workload."""
+    """HBM bytes per step (all of a step's kernels) from the committed
+    rocprofv3 counter summary, if it was taken on the current kernel sources
+    and this workload."""
     path = os.path.join(ROOT, "profiles", f"decode_{config}_counters.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
     m_hash = re.search(r"source-hash:\s*([0-9a-f]+)", text)
-    m_bytes = re.search(r"hbm-bytes-per-launch:\s*([0-9.eE+]+)", text)
+    m_bytes = re.search(r"hbm-bytes-per-step:\s*([0-9.eE+]+)", text)
     if not (m_hash and m_bytes) or m_hash.group(1) != kernel_source_hash():
         return None
     return float(m_bytes.group(1))
@@ -441,29 +442,47 @@ def main(argv=None) -> int:
         decode(i)
     torch.cuda.synchronize()
 
+    # Timed region: K steps back to back, one HIP event pair on the library's
+    # stream around them (an event pair around every step would add its own
+    # gaps between the launches: ~7 us per step measured).
     K = args.steps
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(K)]
+    region = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    region[0].record(stream)
     for i in range(K):
         j = args.warmup + i
+        if not (args.decode_only or fused):
+            reshape(j)
+        decode(j)
+    region[1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    region_ms = region[0].elapsed_time(region[1])
+    # Spread of single calls, from a separate pass with an event pair around
+    # each call (not the timed region).
+    nspread = min(K, 50)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(nspread)]
+    for i in range(nspread):
+        j = args.warmup + K + i
         if not (args.decode_only or fused):
             reshape(j)
         ev[i][0].record(stream)
         decode(j)
         ev[i][1].record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     dec_ms = np.array([a.elapsed_time(b) for a, b in ev])
 
     ab = W.algorithmic_bytes(w, unique=True)
     step_bytes = ab["total"] + (0 if args.decode_only else W.reshape_bytes(w))
     ms_per_step = wall * 1e3 / K
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
-    dec_avg = float(dec_ms.mean())
-    # the timed launch: decode alone, or decode with the KV write inside it
-    launch_bytes = ab["total"] + (W.reshape_bytes(w) if fused else 0)
+    # Roofline of the step's launches over the timed region: one call of
+    # pa_reshape_and_decode (the KV write inside the decode kernel), or the
+    # KV-write kernel and the decode call.
+    dec_avg = region_ms / K
+    launch_bytes = step_bytes
     achieved = launch_bytes / (dec_avg * 1e-3) / 1e9
     traffic = stored_traffic(args.config)
 
@@ -501,16 +520,23 @@ def main(argv=None) -> int:
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic,
-                     "kernel": ("pa_paged_attention_decode_cascade (shared-prefix kernel + "
+                     "kernel": ("pa_paged_attention_decode_cascade (KV-write kernel, "
+                                "shared-prefix kernel, decode kernel)" if cascade and
+                                not args.decode_only else
+                                "pa_paged_attention_decode_cascade (shared-prefix kernel + "
                                 "decode kernel)" if cascade else
                                 ("pa_reshape_and_decode (decode kernel with the KV write"
-                                 if fused else "pa_paged_attention_decode (decode kernel")
+                                 if fused else "pa_paged_attention_decode (decode kernel"
+                                 if args.decode_only else
+                                 "pa_reshape_and_cache + pa_paged_attention_decode (KV-write "
+                                 "kernel, decode kernel")
                                 + (" + split-K reduce" if part and w.max_context_len > part
                                    else "") + ")"),
                      "launch_us_avg": round(dec_avg * 1e3, 2),
-                     "launch_us_p10": round(float(np.percentile(dec_ms, 10)) * 1e3, 2),
-                     "launch_us_p90": round(float(np.percentile(dec_ms, 90)) * 1e3, 2),
-                     "algorithmic_bytes_per_launch": launch_bytes},
+                     "timing": "HIP events around the timed region / steps",
+                     "single_call_us_p10": round(float(np.percentile(dec_ms, 10)) * 1e3, 2),
+                     "single_call_us_p90": round(float(np.percentile(dec_ms, 90)) * 1e3, 2),
+                     "algorithmic_bytes_per_step": launch_bytes},
     }
     if args.query_len > 0:
         result["multi_query"] = multi_query_bench(args, w, d, pools, part, stream)
