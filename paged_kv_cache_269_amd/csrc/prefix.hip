@@ -32,25 +32,39 @@ namespace {
 
 constexpr int kMinPrefixBlocks = 4;
 
+// Most sequences in one run (16 query rows, at least one head each).
+constexpr int kMaxRunSeqs = 16;
+
 // Leading full blocks that sequences s0 .. s0+ns-1 all map to the same
 // physical blocks (0 when fewer than kMinPrefixBlocks or ns < 2).  Every wave
-// computes it: the members' lengths and the first 128 entries of their table
-// rows are loaded together (one round trip), mismatches found with ballots;
-// longer shared parts continue 64 entries at a time.  No barrier is needed.
+// computes it: the members' lengths and the first 128 entries of all their
+// table rows are loaded together (one round trip: every load is issued
+// before the first compare; rows past the run repeat its last member),
+// mismatches found with ballots; longer shared parts continue 64 entries at
+// a time.  No barrier is needed.
 __device__ __forceinline__ int group_prefix_blocks(const DecodeArgs& a, int s0, int ns) {
   if (ns < 2) return 0;
   const int lane = threadIdx.x & 63;
   const int M = a.max_blocks_per_seq;
   const int32_t* r0 = a.block_tables + (int64_t)s0 * M;
   const int lb = lane < ns ? clamp_len(a, s0 + lane) / kBlockSize : INT_MAX;
-  const int ref0 = lane < M ? r0[lane] : 0;
-  const int ref1 = 64 + lane < M ? r0[64 + lane] : 0;
-  bool d0 = false, d1 = false;
-  for (int i = 1; i < ns; ++i) {
-    const int32_t* r = r0 + (int64_t)i * M;
-    if (lane < M) d0 |= r[lane] != ref0;
-    if (64 + lane < M) d1 |= r[64 + lane] != ref1;
+  const int c0 = min(lane, M - 1), c1 = min(64 + lane, M - 1);  // entries, clamped into the row
+  const int ref0 = r0[c0], ref1 = r0[c1];
+  int e0[kMaxRunSeqs - 1], e1[kMaxRunSeqs - 1];
+#pragma unroll
+  for (int i = 1; i < kMaxRunSeqs; ++i) {
+    const int32_t* r = r0 + (int64_t)min(i, ns - 1) * M;
+    e0[i - 1] = r[c0];
+    e1[i - 1] = r[c1];
   }
+  bool d0 = false, d1 = false;
+#pragma unroll
+  for (int i = 1; i < kMaxRunSeqs; ++i) {
+    d0 |= e0[i - 1] != ref0;
+    d1 |= e1[i - 1] != ref1;
+  }
+  d0 = d0 && lane < M;
+  d1 = d1 && 64 + lane < M;
   int full = M;  // whole blocks in every member's context
   for (int i = 0; i < ns; ++i) full = min(full, __builtin_amdgcn_readlane(lb, i));
   if (full < kMinPrefixBlocks) return 0;
