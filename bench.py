@@ -139,7 +139,8 @@ def decode_loop(args, w, dev):
     appends one token to every sequence (the manager hands out the slots and
     takes a new block at each 16-token boundary) and exports the block tables
     and lengths into a pinned host buffer; the device part -- one copy of that
-    buffer, the KV write and the decode -- is a captured HIP graph, replayed
+    buffer and one pa_reshape_and_decode call (KV write inside the decode
+    launch) -- is a captured HIP graph, replayed
     once per step.  Two buffer/graph sets alternate so that the host fills one
     while the device reads the other.  The workload's context lengths are the
     prompts; their K/V is whatever the freshly allocated pool holds (timing
@@ -185,9 +186,9 @@ def decode_loop(args, w, dev):
 
     def device_part(st, stream):
         st["d"].copy_(st["h"], non_blocking=True)
-        pa.reshape_and_cache(knew, vnew, kc, vc, st["d_slots"], stream=stream)
-        pa.paged_attention_decode(out, q, kc, vc, st["d_bt"], st["d_cl"], w.scale, maxlen,
-                                  partition_size=w.partition_size, workspace=ws, stream=stream)
+        pa.reshape_and_decode(out, q, knew, vnew, kc, vc, st["d_slots"], st["d_bt"], st["d_cl"],
+                              w.scale, maxlen, partition_size=w.partition_size, workspace=ws,
+                              stream=stream)
 
     # fill both sets once (valid tables) and capture one graph per set
     for st in sets:
@@ -246,7 +247,7 @@ def decode_loop(args, w, dev):
             "device_graph_us_per_step": round(dev_us, 2),
             "pool_blocks": N,
             "note": "per step: block-manager appends + table export on the host, then one HIP "
-                    "graph (packed H2D copy, reshape_and_cache, decode)"}
+                    "graph (packed H2D copy, pa_reshape_and_decode)"}
 
 
 def block_ops(w, dev):

@@ -56,15 +56,21 @@ def test_multistep_decode_with_block_manager(cuda, dtype, Hq, Hkv):
     W._nan_fill(kh, dtype, slice(None))
     W._nan_fill(vh, dtype, slice(None))
     kd, vd = to_dev(kh, dtype, cuda), to_dev(vh, dtype, cuda)
+    # a second device pool whose decode-step tokens go in through the one-call
+    # step (pa_reshape_and_decode); prompts are written to both pools
+    kd2, vd2 = kd.clone(), vd.clone()
 
-    def write(slots):
-        """New K/V rows at `slots` on both sides."""
+    def write(slots, fused_pool_too=True):
+        """New K/V rows at `slots` on both sides; returns the device rows."""
         k = rand_rows(rng, (len(slots), Hkv, D), dtype)
         v = rand_rows(rng, (len(slots), Hkv, D), dtype)
         sl = np.asarray(slots, np.int64)
-        pa.reshape_and_cache(to_dev(k, dtype, cuda), to_dev(v, dtype, cuda), kd, vd,
-                             torch.from_numpy(sl).to(cuda))
+        kdev, vdev, sdev = to_dev(k, dtype, cuda), to_dev(v, dtype, cuda), torch.from_numpy(sl).to(cuda)
+        pa.reshape_and_cache(kdev, vdev, kd, vd, sdev)
+        if fused_pool_too:
+            pa.reshape_and_cache(kdev, vdev, kd2, vd2, sdev)
         oracle.reshape_and_cache(k, v, kh, vh, sl, dtype)
+        return kdev, vdev, sdev
 
     def prompt(rid, n):
         write([bm.append(rid)[0] for _ in range(n)])
@@ -90,12 +96,15 @@ def test_multistep_decode_with_block_manager(cuda, dtype, Hq, Hkv):
             bm.allocate(5, 0)          # takes blocks request 3 left
             prompt(5, 50)
             live.append(5)
-        write([bm.append(r)[0] for r in live])
+        knew, vnew, snew = write([bm.append(r)[0] for r in live], fused_pool_too=False)
         bt, cl = bm.block_tables(live, M, pad=0)
         q = rand_rows(rng, (len(live), Hq, D), dtype)
         qd, btd, cld = to_dev(q, dtype, cuda), torch.from_numpy(bt).to(cuda), torch.from_numpy(cl).to(cuda)
         out = torch.empty_like(qd)
         pa.paged_attention_decode(out, qd, kd, vd, btd, cld, scale, int(cl.max()), partition_size=0)
+        out_f = torch.empty_like(qd)
+        pa.reshape_and_decode(out_f, qd, knew, vnew, kd2, vd2, snew, btd, cld, scale,
+                              int(cl.max()), partition_size=0)
         out_c = torch.empty_like(qd)
         pa.paged_attention_decode_cascade(out_c, qd, kd, vd, btd, cld, scale, int(cl.max()),
                                           workspace=ws)
@@ -104,20 +113,25 @@ def test_multistep_decode_with_block_manager(cuda, dtype, Hq, Hkv):
         rs_, rh = np.repeat(np.arange(B), Hq), np.tile(np.arange(Hq), B)
         ref, _, _ = oracle.decode_rows(q, kh, vh, bt, cl, scale, dtype, rs_, rh)
         ref = ref.reshape(B, Hq, D)
-        for name, o in (("plain", out), ("cascade", out_c)):
+        for name, o in (("plain", out), ("cascade", out_c), ("one-call step", out_f)):
             got = to_f64(tensor_to_np(o, dtype), dtype)
             check_close(got, ref, dtype, f"step {step} {name}")
         if step % 10 == 0:
             announce("step", step, "lens", cl.tolist(), "free", bm.num_free())
     assert bm.seq_len(5) == 50 + 18 and bm.seq_len(0) == 80 + 30
+    # both pools hold the same bits (the one-call step's writes included)
+    assert torch.equal(kd.view(torch.int16), kd2.view(torch.int16))
+    assert torch.equal(vd.view(torch.int16), vd2.view(torch.int16))
     bm.close()
 
 
-def test_decode_step_graph_replays_match_eager(cuda):
+@pytest.mark.parametrize("one_call", [False, True])
+def test_decode_step_graph_replays_match_eager(cuda, one_call):
     """A decode step captured as a HIP graph (packed host-to-device copy of
-    slots, tables and lengths, KV write, decode) replayed step after step,
-    with eager work and synchronisations in between: every replay equals the
-    eager decode of the same step, bit for bit, and the oracle."""
+    slots, tables and lengths, KV write, decode -- as two calls or as one
+    pa_reshape_and_decode call) replayed step after step, with eager work and
+    synchronisations in between: every replay equals the eager decode of the
+    same step, bit for bit, and the oracle."""
     import paged_kv_cache_269_amd as pa
     dtype, Hq, Hkv, D, N, M = "bf16", 16, 2, 128, 64, 16
     rng = np.random.default_rng(5)
@@ -144,9 +158,13 @@ def test_decode_step_graph_replays_match_eager(cuda):
 
     def device_part(stream):
         dvb.copy_(h, non_blocking=True)
-        pa.reshape_and_cache(kn, vn, kd, vd, d_slots, stream=stream)
-        pa.paged_attention_decode(out, q, kd, vd, d_bt, d_cl, scale, maxlen, partition_size=0,
-                                  stream=stream)
+        if one_call:
+            pa.reshape_and_decode(out, q, kn, vn, kd, vd, d_slots, d_bt, d_cl, scale, maxlen,
+                                  partition_size=0, stream=stream)
+        else:
+            pa.reshape_and_cache(kn, vn, kd, vd, d_slots, stream=stream)
+            pa.paged_attention_decode(out, q, kd, vd, d_bt, d_cl, scale, maxlen,
+                                      partition_size=0, stream=stream)
 
     bm.block_tables(ids, M, 0, out=(bt, cl))
     slots[:] = -1
@@ -161,7 +179,7 @@ def test_decode_step_graph_replays_match_eager(cuda):
         device_part(torch.cuda.current_stream())
     torch.cuda.synchronize()
     for step in range(6):
-        announce("graph step", step)
+        announce("graph step", step, "one call" if one_call else "two calls")
         bm.append_batch(ids, slots)
         bm.block_tables(ids, M, 0, out=(bt, cl))
         g.replay()
