@@ -257,14 +257,15 @@ __global__ __launch_bounds__(NW * 64, 2) void multi_query_kernel(MultiQueryArgs 
   });
 }
 
-// LDS of the wide kernel: per buffer and wave, one staged tile (K in the
-// padded staging layout, V as the loading wave's registers) and its token
-// count.
+// LDS of the wide kernel: per buffer and wave, one staged tile and its
+// token count.  K and V rows both keep their 16-byte chunks permuted within
+// the row (kswz), so the column-wise operand reads of 16 rows spread over
+// the banks.
 template <int D, typename VT, int NW>
 struct WideLds {
   struct Tile {
     u32x4 k[kBlockSize * D / 8];  // 16-byte chunk c of row r at r * D/8 + (c ^ r % (D/8))
-    VT v[4][64];                  // rows in order: lane l's V slice of rows g + 4e at [e][l]
+    u32x4 v[kBlockSize * D / 8];  // the same layout for V
   };
   Tile t[2][NW];
   int lim[2][NW];
@@ -291,6 +292,23 @@ __device__ __forceinline__ void load16_to_lds(Rsrc r, u32x4* dst, int voffset) {
 #endif
 }
 
+// Transposing LDS read (gfx950): within each 16-lane group, lane i receives
+// [x_0[i % 4], x_1[i % 4], x_2[i % 4], x_3[i % 4]] where x_k is the 8 bytes
+// (four 16-bit elements) that lane 4k + i / 4 of the group addresses -- the
+// lane layout was checked on the device.  It turns four token rows into
+// one column of four tokens per lane, the B operand of the P.V products.
+__device__ __forceinline__ u32x2 lds_read_tr16(const void* p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4i16*)(const_cast<void*>(p)));
+  return __builtin_bit_cast(u32x2, v);
+#else
+  (void)p;
+  return u32x2{0u, 0u};
+#endif
+}
+
 // Wait for this wave's loads into LDS to land.
 __device__ __forceinline__ void wait_lds_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
@@ -309,7 +327,6 @@ __device__ __forceinline__ void fold_group(MfmaState<D> (&st)[RT],
                                            const int (&lims)[NT], int g_first,
                                            float scale_log2, const MfmaLane& ln) {
   using S = MfmaShape<DT, D>;
-  using VT = typename S::VT;
   const int lane = ln.n + 16 * ln.g;
   float sc[RT][NT][4];
 #pragma unroll
@@ -391,11 +408,18 @@ __device__ __forceinline__ void fold_group(MfmaState<D> (&st)[RT],
   // P.V over pairs of tiles: the two tiles' 4 + 4 tokens of a lane are one
   // 8-wide contraction slice of a 16x16x32 product (P and V take the tokens
   // in the same order), half the instructions of two 16x16x16 products.
-  // The V rows are read from LDS in 8-byte halves of the lane's slices
-  // (D = 128: dims EPL*n + 0..3, then + 4..7), which keeps half the V
-  // registers live.
+  // Product jj gives output dims 16 jj + n.  Its V operand -- tokens
+  // g + 4k (k = 0..3) of dim 16 jj + n, per tile -- comes straight out of
+  // LDS through the transposing read: lane 4k + q of a 16-lane group
+  // addresses row g + 4k, dims 16 jj + 4q .. + 3.
   static_assert(NT % 2 == 0, "tiles are folded in pairs");
-  constexpr int HALVES = S::EPL / 4;
+  constexpr int CPR = D / 8;
+  const int tr_row = ln.g + 4 * ((lane & 15) >> 2), tr_q = lane & 3;
+  // byte offset in a tile of this lane's 8 bytes for product jj (kswz layout)
+  auto tr_off = [&](int jj) {
+    const int c = 2 * jj + (tr_q >> 1);
+    return (tr_row * CPR + (c ^ (tr_row % CPR))) * 16 + (tr_q & 1) * 8;
+  };
 #pragma unroll
   for (int t = 0; t < NT; t += 2) {
     u32x4 pp[RT];
@@ -403,28 +427,22 @@ __device__ __forceinline__ void fold_group(MfmaState<D> (&st)[RT],
     for (int r = 0; r < RT; ++r)
       pp[r] = u32x4{pa[r][t][0], pa[r][t][1], pa[r][t + 1][0], pa[r][t + 1][1]};
 #pragma unroll
-    for (int hv = 0; hv < HALVES; ++hv) {
-      u32x2 v0[4], v1[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        v0[e] = reinterpret_cast<const u32x2*>(&tiles[t].v[e][lane])[hv];
-        v1[e] = reinterpret_cast<const u32x2*>(&tiles[t + 1].v[e][lane])[hv];
-        if constexpr (MASKED) {
-          // what the slots past a tile's tokens hold must not reach P.V
-          if (ln.g + 4 * e >= lims[t]) v0[e] = u32x2{0u, 0u};
-          if (ln.g + 4 * e >= lims[t + 1]) v1[e] = u32x2{0u, 0u};
-        }
+    for (int jj = 0; jj < D / 16; ++jj) {
+      u32x2 v0 = lds_read_tr16(reinterpret_cast<const char*>(tiles[t].v) + tr_off(jj));
+      u32x2 v1 = lds_read_tr16(reinterpret_cast<const char*>(tiles[t + 1].v) + tr_off(jj));
+      if constexpr (MASKED) {
+        // what the slots past a tile's tokens hold must not reach P.V:
+        // element k of this lane is token g + 4k
+        const uint32_t m0 = (ln.g < lims[t] ? 0xffffu : 0u) | (ln.g + 4 < lims[t] ? 0xffff0000u : 0u);
+        const uint32_t m1 = (ln.g + 8 < lims[t] ? 0xffffu : 0u) | (ln.g + 12 < lims[t] ? 0xffff0000u : 0u);
+        const uint32_t n0 = (ln.g < lims[t + 1] ? 0xffffu : 0u) | (ln.g + 4 < lims[t + 1] ? 0xffff0000u : 0u);
+        const uint32_t n1 = (ln.g + 8 < lims[t + 1] ? 0xffffu : 0u) | (ln.g + 12 < lims[t + 1] ? 0xffff0000u : 0u);
+        v0 = u32x2{v0[0] & m0, v0[1] & m1};
+        v1 = u32x2{v1[0] & n0, v1[1] & n1};
       }
+      const u32x4 vb{v0[0], v0[1], v1[0], v1[1]};
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int jj = 4 * hv + k;
-        const u32x4 vb{VSlice<4>::half(v0[0], k) | (VSlice<4>::half(v0[1], k) << 16),
-                       VSlice<4>::half(v0[2], k) | (VSlice<4>::half(v0[3], k) << 16),
-                       VSlice<4>::half(v1[0], k) | (VSlice<4>::half(v1[1], k) << 16),
-                       VSlice<4>::half(v1[2], k) | (VSlice<4>::half(v1[3], k) << 16)};
-#pragma unroll
-        for (int r = 0; r < RT; ++r) st[r].o[jj] = mfma_qk<DT>(pp[r], vb, st[r].o[jj]);
-      }
+      for (int r = 0; r < RT; ++r) st[r].o[jj] = mfma_qk<DT>(pp[r], vb, st[r].o[jj]);
     }
   }
 }
@@ -518,7 +536,7 @@ __global__ __launch_bounds__(NW * 64, 2) void multi_query_wide_kernel(MultiQuery
       constexpr int h = Desc::part(jj * 1024);
       const int p = jj * 64 + lane;
       const int r = p / S::CPR, c = (p % S::CPR) ^ (r % S::CPR);
-      const int koff = (r * S::CPR + c) * 16 - h * Desc::HB, voff = p * 16 - h * Desc::HB;
+      const int koff = (r * S::CPR + c) * 16 - h * Desc::HB, voff = koff;  // both kswz
       if (ma.reread) {
         load16_to_lds<PA_SHARED_LOAD_POLICY>(desc.k[h], lds_k[b] + jj * 64, koff);
         load16_to_lds<PA_SHARED_LOAD_POLICY>(desc.v[h], lds_v[b] + jj * 64, voff);
@@ -573,7 +591,7 @@ __global__ __launch_bounds__(NW * 64, 2) void multi_query_wide_kernel(MultiQuery
   }
 
   // Each wave writes its own rows: output row 4g+e of a row tile, dims
-  // EPL*n + jj (the P.V result layout).
+  // 16 jj + n (the P.V result layout).
   static_for<0, RT>([&](auto rc) __attribute__((always_inline)) {
     constexpr int r = decltype(rc)::value;
     if (rows_t[r] == 0) return;
@@ -593,11 +611,11 @@ __global__ __launch_bounds__(NW * 64, 2) void multi_query_wide_kernel(MultiQuery
       if (row_parts <= 1) {
 #pragma unroll
         for (int jj = 0; jj < EPL; ++jj)
-          store_elem<DT>(a.out, orow * D + EPL * ln.n + jj, st[r].o[jj][e] * inv);
+          store_elem<DT>(a.out, orow * D + 16 * jj + ln.n, st[r].o[jj][e] * inv);
       } else {
         const int64_t prow = orow * a.max_partitions + part;
 #pragma unroll
-        for (int jj = 0; jj < EPL; ++jj) a.tmp_out[prow * D + EPL * ln.n + jj] = st[r].o[jj][e] * inv;
+        for (int jj = 0; jj < EPL; ++jj) a.tmp_out[prow * D + 16 * jj + ln.n] = st[r].o[jj][e] * inv;
       }
     }
     // per-row max and sum of the partial, from the lanes holding row n
