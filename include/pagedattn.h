@@ -357,6 +357,19 @@ int pa_validate_tables_host(const int32_t* block_tables, const int32_t* context_
 int pa_validate_slots_host(const int64_t* slot_mapping, int32_t num_tokens,
                            int64_t num_blocks, int32_t block_size);
 
+/*
+ * Host-side check of one decode step for pa_reshape_and_decode (host
+ * pointers; one new token per sequence, slot_mapping [num_seqs]): the tables
+ * and the slots pass pa_validate_tables_host and pa_validate_slots_host, and
+ * no context reads a slot written in this step other than the writer's own
+ * last position context_lens[s] - 1 -- the condition under which the one-call
+ * step equals the KV write followed by the decode.  Returns PA_OK,
+ * PA_ERR_RANGE (first violation), PA_ERR_NULL or PA_ERR_SHAPE.
+ */
+int pa_validate_step_host(const int64_t* slot_mapping, const int32_t* block_tables,
+                          const int32_t* context_lens, int32_t num_seqs,
+                          int32_t max_blocks_per_seq, int64_t num_blocks, int32_t block_size);
+
 /* Static description of a status code. */
 const char* pa_status_string(int status);
 

@@ -50,6 +50,7 @@ EXPORTS = {
     "pa_validate_query_start_host": (ctypes.c_int, [_P, _P, _I32, _I32, _I32]),
     "pa_validate_tables_host": (ctypes.c_int, [_P, _P, _I32, _I32, _I64, _I32]),
     "pa_validate_slots_host": (ctypes.c_int, [_P, _I32, _I64, _I32]),
+    "pa_validate_step_host": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _I64, _I32]),
     "pa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "pa_version": (ctypes.c_char_p, []),
     # host block manager (include/pagedattn_blocks.h)
@@ -430,6 +431,22 @@ def validate_slots_host(slot_mapping, num_blocks: int, block_size: int = 16) -> 
     sm = np.ascontiguousarray(slot_mapping, dtype=np.int64)
     return int(load_library().pa_validate_slots_host(
         sm.ctypes.data_as(ctypes.c_void_p), sm.shape[0], int(num_blocks), block_size))
+
+
+def validate_step_host(slot_mapping, block_tables, context_lens, num_blocks: int,
+                       block_size: int = 16) -> int:
+    """pa_validate_step_host on host arrays (numpy or CPU tensors): whether a
+    decode step meets pa_reshape_and_decode's condition (status code)."""
+    import numpy as np
+    sl = np.ascontiguousarray(np.asarray(slot_mapping, dtype=np.int64))
+    bt = np.ascontiguousarray(np.asarray(block_tables, dtype=np.int32))
+    cl = np.ascontiguousarray(np.asarray(context_lens, dtype=np.int32))
+    if bt.ndim != 2 or bt.shape[0] != cl.shape[0] or sl.shape != cl.shape:
+        raise ValueError("block_tables [B, M], context_lens [B], slot_mapping [B]")
+    return int(load_library().pa_validate_step_host(
+        sl.ctypes.data_as(ctypes.c_void_p), bt.ctypes.data_as(ctypes.c_void_p),
+        cl.ctypes.data_as(ctypes.c_void_p), cl.shape[0], bt.shape[1], int(num_blocks),
+        int(block_size)))
 
 
 class KVCacheExhausted(PagedAttnError):

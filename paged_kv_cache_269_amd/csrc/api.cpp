@@ -7,6 +7,7 @@
 #include <algorithm>
 #include <climits>
 #include <cstdint>
+#include <utility>
 #include <vector>
 
 #include "launch.h"
@@ -482,6 +483,41 @@ int pa_validate_slots_host(const int64_t* slot_mapping, int32_t num_tokens, int6
   }
   std::sort(used.begin(), used.end());
   if (std::adjacent_find(used.begin(), used.end()) != used.end()) return PA_ERR_RANGE;
+  return PA_OK;
+}
+
+int pa_validate_step_host(const int64_t* slot_mapping, const int32_t* block_tables,
+                          const int32_t* context_lens, int32_t num_seqs,
+                          int32_t max_blocks_per_seq, int64_t num_blocks, int32_t block_size) {
+  int rc = pa_validate_tables_host(block_tables, context_lens, num_seqs, max_blocks_per_seq,
+                                   num_blocks, block_size);
+  if (rc != PA_OK) return rc;
+  rc = pa_validate_slots_host(slot_mapping, num_seqs, num_blocks, block_size);
+  if (rc != PA_OK || num_seqs == 0) return rc;
+  // Every (sequence, logical block) of every context, grouped by pool block.
+  std::vector<std::pair<int32_t, int64_t>> reads;  // (pool block, s * M + j)
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    const int64_t nb = ceil_div(context_lens[s], block_size);
+    for (int64_t j = 0; j < nb; ++j)
+      reads.emplace_back(block_tables[(int64_t)s * max_blocks_per_seq + j],
+                         (int64_t)s * max_blocks_per_seq + j);
+  }
+  std::sort(reads.begin(), reads.end());
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    const int64_t slot = slot_mapping[s];
+    if (slot < 0) continue;
+    const int32_t b = (int32_t)(slot / block_size), off = (int32_t)(slot % block_size);
+    const int32_t L = context_lens[s];
+    auto it = std::lower_bound(reads.begin(), reads.end(), std::make_pair(b, INT64_MIN));
+    for (; it != reads.end() && it->first == b; ++it) {
+      const int32_t r = (int32_t)(it->second / max_blocks_per_seq);
+      const int64_t j = it->second % max_blocks_per_seq;
+      const int64_t pos = j * block_size + off;  // position of the slot in r's context
+      if (pos >= context_lens[r]) continue;                // not read by r
+      if (r == s && pos == (int64_t)L - 1) continue;       // the writer's own last position
+      return PA_ERR_RANGE;
+    }
+  }
   return PA_OK;
 }
 

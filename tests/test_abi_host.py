@@ -253,6 +253,37 @@ def test_slot_validator(hiplib):
     assert hiplib.validate_slots_host(np.zeros(0, np.int64), 10) == OK
 
 
+def test_step_validator(hiplib):
+    """pa_validate_step_host: the one-call step's condition -- no context
+    reads a slot written in the step, except the writer's own last position."""
+    from paged_kv_cache_269_amd import workloads as W
+    for name, over in (("tiny", {}), ("llama7b", dict(num_seqs=5, len_lo=1, len_hi=300)),
+                       ("shared_prefix", dict(num_seqs=6, len_lo=20, len_hi=60,
+                                              shared_prefix_blocks=4))):
+        w = W.generate(name, **over)
+        assert hiplib.validate_step_host(w.slot_mapping, w.block_tables, w.context_lens,
+                                         w.num_blocks, w.block_size) == OK, name
+    # hand-built: 3 sequences, 16-token blocks; 0 and 1 share block 7
+    bt = np.array([[7, 2, 0], [7, 3, 0], [5, 0, 0]], np.int32)
+    cl = np.array([20, 18, 16], np.int32)
+    ok = np.array([2 * 16 + 3, 3 * 16 + 1, 5 * 16 + 15], np.int64)  # each one's last position
+    assert hiplib.validate_step_host(ok, bt, cl, 10) == OK
+    assert hiplib.validate_step_host(np.array([-1, -1, -1]), bt, cl, 10) == OK
+    free = ok.copy(); free[2] = 9 * 16 + 4            # a block no context reads
+    assert hiplib.validate_step_host(free, bt, cl, 10) == OK
+    shared = ok.copy(); shared[0] = 7 * 16 + 5        # block 7 is read by sequence 1 as well
+    assert hiplib.validate_step_host(shared, bt, cl, 10) == RANGE
+    own = ok.copy(); own[1] = 3 * 16 + 0              # sequence 1 reads position 16 as context
+    assert hiplib.validate_step_host(own, bt, cl, 10) == RANGE
+    other = ok.copy(); other[2] = 2 * 16 + 1          # inside sequence 0's context
+    assert hiplib.validate_step_host(other, bt, cl, 10) == RANGE
+    dup = ok.copy(); dup[2] = dup[0]                  # two tokens, one slot
+    assert hiplib.validate_step_host(dup, bt, cl, 10) == RANGE
+    assert hiplib.validate_step_host(ok, bt, cl, 6) == RANGE  # block 7 outside the pool
+    tail = ok.copy(); tail[1] = 3 * 16 + 5            # past sequence 1's end: nobody reads it
+    assert hiplib.validate_step_host(tail, bt, cl, 10) == OK
+
+
 def test_binding_refuses_host_tensors(hiplib):
     import torch
     x = torch.zeros(2, 4, 128, dtype=torch.float16)

@@ -78,6 +78,9 @@ def after_write(w):
 def check_case(w, cuda, parts, label):
     """Fused call on fresh inputs for each partition size: pool, oracle,
     two-call form."""
+    import paged_kv_cache_269_amd as pa
+    assert pa.validate_step_host(w.slot_mapping, w.block_tables, w.context_lens, w.num_blocks,
+                                 w.block_size) == 0, f"{label}: not a valid one-call step"
     w2 = after_write(w)
     ref = full_oracle(w2)
     view = np.uint32 if w.dtype == "f32" else np.uint16
