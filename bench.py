@@ -399,8 +399,8 @@ def main(argv=None) -> int:
     out = torch.empty_like(d["q"])
     cascade = bool(w.params.get("cascade")) and part == 0
     # one call per step (KV write inside the decode launch) unless the step
-    # is asked for as two calls, is decode only, or is the cascade form
-    fused = not (args.two_call or args.decode_only or cascade)
+    # is asked for as two calls or is decode only
+    fused = not (args.two_call or args.decode_only)
     if cascade:   # allocated once, outside the timed loop
         ws = pa.cascade_workspace(w.num_seqs, w.num_q_heads, w.head_dim, device=dev)
     else:
@@ -414,7 +414,12 @@ def main(argv=None) -> int:
 
     def decode(i):
         kc, vc = pools[i % len(pools)]
-        if fused:
+        if fused and cascade:
+            pa.reshape_and_decode_cascade(out, d["q"], d["key"], d["value"], kc, vc,
+                                          d["slot_mapping"], d["block_tables"],
+                                          d["context_lens"], w.scale, w.max_context_len,
+                                          workspace=ws, stream=stream)
+        elif fused:
             pa.reshape_and_decode(out, d["q"], d["key"], d["value"], kc, vc, d["slot_mapping"],
                                   d["block_tables"], d["context_lens"], w.scale,
                                   w.max_context_len, partition_size=part, workspace=ws,
@@ -507,7 +512,8 @@ def main(argv=None) -> int:
                    "context_len_mean": float(w.context_lens.mean()),
                    "context_len_max": int(w.max_context_len), "num_blocks": w.num_blocks,
                    "pool_copies": len(pools),
-                   "entry": ("pa_reshape_and_decode" if fused else
+                   "entry": ("pa_reshape_and_decode_cascade" if fused and cascade else
+                             "pa_reshape_and_decode" if fused else
                              "pa_paged_attention_decode_cascade" if cascade
                              else "pa_paged_attention_decode"),
                    "step": ("decode" if args.decode_only else
@@ -521,7 +527,9 @@ def main(argv=None) -> int:
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic,
-                     "kernel": ("pa_paged_attention_decode_cascade (KV-write kernel, "
+                     "kernel": ("pa_reshape_and_decode_cascade (KV-write kernel, "
+                                "shared-prefix kernel, decode kernel)" if cascade and fused else
+                                "pa_paged_attention_decode_cascade (KV-write kernel, "
                                 "shared-prefix kernel, decode kernel)" if cascade and
                                 not args.decode_only else
                                 "pa_paged_attention_decode_cascade (shared-prefix kernel + "

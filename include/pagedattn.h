@@ -220,6 +220,25 @@ int pa_paged_attention_decode_cascade(void* out, const void* q, const void* k_ca
                                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * The one-call step of the cascade entry point: each sequence's new token
+ * (key, value [num_seqs, num_kv_heads, head_dim], slot_mapping [num_seqs])
+ * written into the caches, then pa_paged_attention_decode_cascade -- the
+ * same two steps enqueued by one call (the KV-write kernel runs first: after
+ * the shared-prefix pass the decode items are short, and writing inside them
+ * measured slower), so the result is the two calls' for any input.  Other
+ * arguments, workspace and errors as for pa_paged_attention_decode_cascade;
+ * key, value and slot_mapping must not be NULL when num_seqs > 0.
+ */
+int pa_reshape_and_decode_cascade(void* out, const void* q, const void* key, const void* value,
+                                  void* k_cache, void* v_cache, const int64_t* slot_mapping,
+                                  const int32_t* block_tables, const int32_t* context_lens,
+                                  int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                  int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                                  int64_t num_blocks, float scale, int32_t dtype,
+                                  int32_t max_context_len, void* workspace, size_t workspace_bytes,
+                                  void* stream);
+
+/*
  * Workspace bytes of pa_paged_attention_decode_cascade: one int32 per
  * sequence, and per (sequence, query head) row two floats plus head_dim
  * floats, each array 256-byte aligned.  Returns 0 for invalid arguments.

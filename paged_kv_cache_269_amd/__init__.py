@@ -25,6 +25,7 @@ from ._binding import (  # noqa: F401
     paged_attention_reduce,
     reshape_and_cache,
     reshape_and_decode,
+    reshape_and_decode_cascade,
     status_string,
     swap_blocks,
     swap_blocks_mapped,
@@ -42,7 +43,8 @@ __all__ = [
     "cascade_workspace_bytes", "copy_blocks", "decode_workspace", "decode_workspace_bytes",
     "lib_path", "load_library", "multi_query_workspace", "multi_query_workspace_bytes",
     "paged_attention_decode", "paged_attention_decode_cascade", "paged_attention_multi_query",
-    "paged_attention_reduce", "reshape_and_cache", "reshape_and_decode", "status_string",
+    "paged_attention_reduce", "reshape_and_cache", "reshape_and_decode", "reshape_and_decode_cascade",
+    "status_string",
     "swap_blocks",
     "swap_blocks_mapped",
     "validate_copy_host", "validate_query_start_host", "validate_slots_host", "validate_step_host",

@@ -43,6 +43,9 @@ EXPORTS = {
                                                          _I32, _I32, _I32, _I32, _I64, _F32,
                                                          _I32, _I32, _P, _SZ, _P]),
     "pa_cascade_workspace_bytes": (ctypes.c_size_t, [_I32, _I32, _I32]),
+    "pa_reshape_and_decode_cascade": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I32,
+                                                     _I32, _I32, _I32, _I32, _I32, _I64, _F32,
+                                                     _I32, _I32, _P, _SZ, _P]),
     "pa_paged_attention_multi_query": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I32, _I32,
                                                       _I32, _I32, _I32, _I32, _I32, _I64, _F32,
                                                       _I32, _I32, _I32, _I32, _P, _SZ, _P]),
@@ -270,6 +273,38 @@ def paged_attention_decode_cascade(out, q, k_cache, v_cache, block_tables, conte
         _dev_ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
         _stream_handle(stream))
     _check("pa_paged_attention_decode_cascade", rc)
+
+
+def reshape_and_decode_cascade(out, q, key, value, k_cache, v_cache, slot_mapping, block_tables,
+                               context_lens, scale: float, max_context_len: int, workspace=None,
+                               stream=None) -> None:
+    """The cascade entry point's one-call step: reshape_and_cache of each
+    sequence's new token (key, value [B, Hkv, D], slot_mapping [B]) inside
+    paged_attention_decode_cascade (pa_reshape_and_decode_cascade)."""
+    import torch
+    B, Hq, D = q.shape
+    N, Hkv, bs, D2 = k_cache.shape
+    if out.shape != q.shape or D2 != D or v_cache.shape != k_cache.shape:
+        raise ValueError("shape mismatch between q, out and the caches")
+    if key.shape != (B, Hkv, D) or value.shape != key.shape or slot_mapping.shape != (B,):
+        raise ValueError("key/value must be [num_seqs, num_kv_heads, head_dim], "
+                         "slot_mapping [num_seqs]")
+    if not (q.dtype == out.dtype == key.dtype == value.dtype == k_cache.dtype == v_cache.dtype):
+        raise TypeError("q, out, key, value and caches must share one element type")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.shape != (B,):
+        raise ValueError("block_tables must be [num_seqs, max_blocks], context_lens [num_seqs]")
+    if workspace is None:
+        workspace = cascade_workspace(B, Hq, D, q.device)
+    rc = load_library().pa_reshape_and_decode_cascade(
+        _dev_ptr(out, "out"), _dev_ptr(q, "q"), _dev_ptr(key, "key"), _dev_ptr(value, "value"),
+        _dev_ptr(k_cache, "k_cache"), _dev_ptr(v_cache, "v_cache"),
+        _dev_ptr(slot_mapping, "slot_mapping", torch.int64),
+        _dev_ptr(block_tables, "block_tables", torch.int32),
+        _dev_ptr(context_lens, "context_lens", torch.int32), B, Hq, Hkv, D, bs,
+        block_tables.shape[1], N, float(scale), _dtype_code(q), int(max_context_len),
+        _dev_ptr(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _stream_handle(stream))
+    _check("pa_reshape_and_decode_cascade", rc)
 
 
 def multi_query_workspace_bytes(num_query_tokens: int, num_q_heads: int, head_dim: int,

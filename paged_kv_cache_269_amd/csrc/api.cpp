@@ -156,6 +156,23 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   // Grouped heads share every K/V tile: a matrix-core product pays off from
   // two heads up.  Single heads and fp32 stay on the vector ALU.
   const bool use_mfma = dtype != PA_F32 && group >= PA_MFMA_MIN_GROUP;
+  if (new_slots != nullptr) {
+    // New tokens' K/V: written by the decode kernel itself, except on the
+    // streaming kernel and in the cascade form, which are preceded by the
+    // KV-write kernel (the cascade's short items after the shared-prefix
+    // pass measured 1.3% slower doing the write themselves).
+    if ((use_mfma && pa::decode_mfma_streams(a)) || cascade) {
+      if (pa::launch_reshape_and_cache(new_k, new_v, const_cast<void*>(k_cache),
+                                       const_cast<void*>(v_cache), new_slots, num_seqs,
+                                       num_kv_heads, head_dim, elem_bytes(dtype), block_size,
+                                       num_blocks, st) != hipSuccess)
+        return PA_ERR_LAUNCH;
+    } else {
+      a.new_k = new_k;
+      a.new_v = new_v;
+      a.new_slots = new_slots;
+    }
+  }
   if (cascade && dtype != PA_F32 && group <= kCascadeMaxGroup && num_seqs >= 2 &&
       block_size == kBlock) {
     // Shared-prefix pass first; the decode kernel then covers each
@@ -169,21 +186,6 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
     a.prefix_l = po.l;
     a.prefix_o = po.o;
     if (pa::launch_prefix(a, po, dtype, head_dim, st) != hipSuccess) return PA_ERR_LAUNCH;
-  }
-  if (new_slots != nullptr) {
-    // New tokens' K/V: written by the decode kernel itself, except on the
-    // streaming kernel, which is preceded by the KV-write kernel.
-    if (use_mfma && pa::decode_mfma_streams(a)) {
-      if (pa::launch_reshape_and_cache(new_k, new_v, const_cast<void*>(k_cache),
-                                       const_cast<void*>(v_cache), new_slots, num_seqs,
-                                       num_kv_heads, head_dim, elem_bytes(dtype), block_size,
-                                       num_blocks, st) != hipSuccess)
-        return PA_ERR_LAUNCH;
-    } else {
-      a.new_k = new_k;
-      a.new_v = new_v;
-      a.new_slots = new_slots;
-    }
   }
   hipError_t e = use_mfma ? pa::launch_decode_mfma(a, dtype, head_dim, st)
                           : pa::launch_decode_valu(a, dtype, head_dim, st);
@@ -277,6 +279,21 @@ int pa_reshape_and_decode(void* out, const void* q, const void* key, const void*
                      num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks, scale,
                      dtype, partition_size, max_context_len, workspace, workspace_bytes, stream,
                      false, key, value, slot_mapping);
+}
+
+int pa_reshape_and_decode_cascade(void* out, const void* q, const void* key, const void* value,
+                                  void* k_cache, void* v_cache, const int64_t* slot_mapping,
+                                  const int32_t* block_tables, const int32_t* context_lens,
+                                  int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                  int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                                  int64_t num_blocks, float scale, int32_t dtype,
+                                  int32_t max_context_len, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+  if (num_seqs > 0 && (!key || !value || !slot_mapping)) return PA_ERR_NULL;
+  return decode_impl(out, q, k_cache, v_cache, block_tables, context_lens, num_seqs, num_q_heads,
+                     num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks, scale,
+                     dtype, 0, max_context_len, workspace, workspace_bytes, stream, true, key,
+                     value, slot_mapping);
 }
 
 size_t pa_cascade_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim) {

@@ -193,3 +193,67 @@ def test_fused_slots_elsewhere(cuda):
         assert np.array_equal(vc[blk, :, off], value[s].view(np.uint16))
     # the padded sequence's free block is untouched (still the generator's NaN)
     assert np.isnan(tensor_to_np(run.dev["k_cache"], w.dtype)[free[1]].astype(np.float32)).all()
+
+
+def cascade_one_call(run, ws=None):
+    import paged_kv_cache_269_amd as pa
+    w, d = run.w, run.dev
+    out = torch.empty_like(d["q"])
+    pa.reshape_and_decode_cascade(out, d["q"], d["key"], d["value"], d["k_cache"], d["v_cache"],
+                                  d["slot_mapping"], d["block_tables"], d["context_lens"], w.scale,
+                                  w.max_context_len, workspace=ws)
+    torch.cuda.synchronize()
+    return out
+
+
+def cascade_two_calls(w, cuda):
+    import paged_kv_cache_269_amd as pa
+    run = Run(w, cuda)
+    run.reshape()
+    d = run.dev
+    out = torch.empty_like(d["q"])
+    pa.paged_attention_decode_cascade(out, d["q"], d["k_cache"], d["v_cache"], d["block_tables"],
+                                      d["context_lens"], w.scale, w.max_context_len)
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("case", [
+    ("shared_prefix", dict(num_seqs=9)),                                    # MHA: vector path
+    ("shared_prefix", dict(num_seqs=12, num_q_heads=32, num_kv_heads=8)),   # G = 4
+    ("shared_prefix", dict(num_seqs=10, num_q_heads=64, num_kv_heads=8, dtype="f16",
+                           len_lo=1, len_hi=40)),                          # G = 8, short suffixes
+    ("shared_prefix", {}),                                                  # full size
+])
+def test_fused_cascade(cuda, case):
+    """pa_reshape_and_decode_cascade on shared-prefix batches (new-token slots
+    hold NaN before the call): pool equal to the oracle's write, output
+    bit-identical to the KV-write kernel + cascade call and within tolerance
+    of the oracle (all rows, or a sample at full size)."""
+    import paged_kv_cache_269_amd as pa
+    name, over = case
+    announce("fused cascade", name, over)
+    w = W.generate(name, **over)
+    assert pa.validate_step_host(w.slot_mapping, w.block_tables, w.context_lens, w.num_blocks,
+                                 w.block_size) == 0
+    run = Run(w, cuda)
+    out = cascade_one_call(run)
+    base = cascade_two_calls(w, cuda)
+    view = np.uint32 if w.dtype == "f32" else np.uint16
+    got_raw = tensor_to_np(out, w.dtype)
+    assert np.array_equal(got_raw.view(view), tensor_to_np(base, w.dtype).view(view)), \
+        "differs from the two-call form"
+    w2 = after_write(w)
+    kc, vc = pool_bits(run, w)
+    assert np.array_equal(kc, w2.k_cache.view(view)) and np.array_equal(vc, w2.v_cache.view(view))
+    B, Hq = w.num_seqs, w.num_q_heads
+    if B * Hq <= 1024:
+        ref = full_oracle(w2)
+        stats = check_close(to_f64(got_raw, w.dtype), ref, w.dtype, f"cascade {over}")
+    else:
+        rng = np.random.default_rng(9)
+        flat = rng.choice(B * Hq, size=64, replace=False)
+        seqs, heads = flat // Hq, flat % Hq
+        stats = check_close(to_f64(got_raw[seqs, heads], w.dtype), oracle_rows(w2, seqs, heads),
+                            w.dtype, "cascade full size")
+    announce(stats)
