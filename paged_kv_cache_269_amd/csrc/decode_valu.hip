@@ -26,6 +26,11 @@
 // Tail tokens (>= context length) of the last block are removed by
 // selection, never by multiplying, so whatever they hold (NaN included)
 // cannot reach the result.
+// One-call decode step (DecodeArgs::new_slots set): the new token of each
+// sequence is written by the item that owns its KV head's last partition,
+// and every item whose context ends with that slot takes the row from
+// registers instead of the cache (same page §1.1: o_t attends over K_{1:t}
+// with token t included), so no item waits for the write.
 #include <type_traits>
 
 #include "common.h"
