@@ -69,14 +69,23 @@ def parse_args(argv=None):
     return ap.parse_args(argv)
 
 
+def _code_only(text: str) -> str:
+    """C++ source without comments and with whitespace runs collapsed (string
+    literals in these sources hold no comment markers)."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_hash() -> str:
-    """Hash of the decode kernel sources, to tell whether stored counters
-    still describe the code being run."""
+    """Hash of the decode kernel sources' code (comments and layout
+    ignored), to tell whether stored counters still describe the code being
+    run."""
     h = hashlib.sha256()
     for f in ("common.h", "items.h", "launch.h", "mfma_tile.h", "decode_valu.hip",
               "decode_mfma.hip", "prefix.hip", "reduce.hip", "reshape_and_cache.hip", "api.cpp"):
-        with open(os.path.join(ROOT, "paged_kv_cache_269_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "paged_kv_cache_269_amd", "csrc", f)) as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 
