@@ -114,12 +114,12 @@ def cpu_baseline(w, target_s: float):
     threads = oracle.max_threads()
     Hq = w.num_q_heads
 
-    def run(nseq):
+    def run(nseq, nthreads=threads):
         seqs = np.repeat(np.arange(nseq), Hq)
         heads = np.tile(np.arange(Hq), nseq)
         t0 = time.perf_counter()
         oracle.decode_rows(w.q, w.k_cache, w.v_cache, w.block_tables, w.context_lens, w.scale,
-                           w.dtype, seqs, heads, num_threads=threads)
+                           w.dtype, seqs, heads, num_threads=nthreads)
         return time.perf_counter() - t0
 
     t1 = run(1)
@@ -137,10 +137,27 @@ def cpu_baseline(w, target_s: float):
         kv = (prefix + int((sub_lens - prefix).sum())) * per_tok
     else:
         kv = int(sub_lens.sum()) * per_tok
-    return {"value": round(kv / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "seqs_per_s": round(n / dt, 3), "seconds": round(dt, 3),
-            "sample": f"first {n} of {w.num_seqs} sequences, all {Hq} query heads, "
-                      f"float64 C oracle with OpenMP, median of {reps} run(s)"}
+    result = {"value": round(kv / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
+              "kind": "oracle", "seqs_per_s": round(n / dt, 3), "seconds": round(dt, 3),
+              "sample": f"first {n} of {w.num_seqs} sequences, all {Hq} query heads, "
+                        f"float64 C oracle with OpenMP, median of {reps} run(s)",
+              "cpu_model": _cpu_model()}
+    if w.name in ("tiny", "llama7b") and threads > 1:
+        # the same sample on one thread, for the two smallest workloads
+        dt1 = run(n, 1)
+        result["single_thread_value"] = round(kv / dt1 / 1e9, 4)
+    return result
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def decode_loop(args, w, dev):
@@ -552,6 +569,7 @@ def main(argv=None) -> int:
                                    else "") + ")"),
                      "launch_us_avg": round(dec_avg * 1e3, 2),
                      "timing": "HIP events around the timed region / steps",
+                     "single_call_us_median": round(float(np.median(dec_ms)) * 1e3, 2),
                      "single_call_us_p10": round(float(np.percentile(dec_ms, 10)) * 1e3, 2),
                      "single_call_us_p90": round(float(np.percentile(dec_ms, 90)) * 1e3, 2),
                      "algorithmic_bytes_per_step": launch_bytes},
