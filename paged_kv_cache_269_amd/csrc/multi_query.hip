@@ -37,7 +37,12 @@ namespace {
 // Workgroup shape: waves and tiles in flight per wave.
 constexpr int kMqWaves = 4;
 constexpr int kMqDepth = 2;
-constexpr int kFoldTiles = 2;  // staged tiles folded together (wide items)
+// Staged tiles a wave of a wide item folds together (fold_group): four with
+// one row tile per wave (64-row items: 306 against 314 us on GQA with 8 new
+// tokens), two with two row tiles (four spill registers there: 412 against
+// 374-380 us with 16 new tokens).
+template <int RT>
+constexpr int kFoldTiles = RT == 1 ? 4 : 2;
 
 // Fold staged tile jt (`limit` tokens) into a wave's RT row tiles, one row
 // tile at a time (folding them side by side needs more registers than two
@@ -453,7 +458,7 @@ __device__ __forceinline__ void fold_group(MfmaState<D> (&st)[RT],
 // loaded once per item, each wave loading one tile of every group of NW
 // straight into double-buffered LDS (buffer loads with the LDS destination:
 // no registers hold tiles in flight; one barrier per group), and read by
-// all waves kFoldTiles at a time (fold_group: one max reduction and rescale
+// all waves kFoldTiles<RT> at a time (fold_group: one max reduction and rescale
 // test per run of tiles, row tiles interleaved).  A wave's rows are
 // complete in its registers at the end: no merge.
 template <int DT, int D, int NW, int BS, int RT>
@@ -574,14 +579,16 @@ __global__ __launch_bounds__(NW * 64, 2) void multi_query_wide_kernel(MultiQuery
       }
       // the group in runs of FT tiles (registers: FT * 16 scores per row tile)
       if (any) {
-        static_for<0, NW / kFoldTiles>([&](auto hc) __attribute__((always_inline)) {
-          constexpr int t0 = decltype(hc)::value * kFoldTiles;
-          const int(&lh)[kFoldTiles] = *reinterpret_cast<const int(*)[kFoldTiles]>(&lims[t0]);
+        constexpr int FT = kFoldTiles<RT>;
+        static_assert(NW % FT == 0, "a group is folded in whole runs");
+        static_for<0, NW / FT>([&](auto hc) __attribute__((always_inline)) {
+          constexpr int t0 = decltype(hc)::value * FT;
+          const int(&lh)[FT] = *reinterpret_cast<const int(*)[FT]>(&lims[t0]);
           if (whole)
-            fold_group<DT, D, kFoldTiles, RT, false>(st, qb, pos_n, &sm.t[b][t0], lh,
+            fold_group<DT, D, FT, RT, false>(st, qb, pos_n, &sm.t[b][t0], lh,
                                                      g_first + t0 * kBlockSize, a.scale_log2, ln);
           else
-            fold_group<DT, D, kFoldTiles, RT, true>(st, qb, pos_n, &sm.t[b][t0], lh,
+            fold_group<DT, D, FT, RT, true>(st, qb, pos_n, &sm.t[b][t0], lh,
                                                     g_first + t0 * kBlockSize, a.scale_log2, ln);
         });
       }
