@@ -290,3 +290,17 @@ def test_binding_refuses_host_tensors(hiplib):
     kc = torch.zeros(3, 4, 16, 128, dtype=torch.float16)
     with pytest.raises(ValueError):
         hiplib.reshape_and_cache(x, x, kc, kc, torch.zeros(2, dtype=torch.int64))
+    # the one-call steps check shapes, then refuse host tensors, before any launch
+    q = torch.zeros(2, 4, 128, dtype=torch.float16)
+    bt = torch.zeros(2, 3, dtype=torch.int32)
+    cl = torch.ones(2, dtype=torch.int32)
+    sl = torch.zeros(2, dtype=torch.int64)
+    with pytest.raises(ValueError):
+        hiplib.reshape_and_decode(torch.empty_like(q), q, x, x, kc, kc, sl, bt, cl, 0.1, 16,
+                                  partition_size=0)
+    with pytest.raises(ValueError):
+        hiplib.reshape_and_decode_cascade(torch.empty_like(q), q, x, x, kc, kc, sl, bt, cl, 0.1,
+                                          16, workspace=torch.zeros(1 << 16, dtype=torch.uint8))
+    with pytest.raises(ValueError):  # key rows must be [num_seqs, num_kv_heads, head_dim]
+        hiplib.reshape_and_decode(torch.empty_like(q), q, x[:1], x[:1], kc, kc, sl, bt, cl, 0.1, 16,
+                                  partition_size=0)
