@@ -145,7 +145,8 @@ int pa_paged_attention_decode(void* out, const void* q, const void* k_cache,
  * this call, a slot written in this call other than its own last position.
  * The decode kernels then store each new row once and use it from registers
  * where a context ends with it, so no kernel waits for the write; when the
- * precondition does not hold the result is undefined.  The streaming kernel
+ * precondition does not hold the result is undefined (pa_validate_step_host
+ * checks it on host copies of the step).  The streaming kernel
  * (16-token blocks, >= 8 partitions, <= 64 sequences, grouped heads) is
  * preceded by the KV-write kernel instead.
  */
