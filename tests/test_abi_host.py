@@ -304,3 +304,51 @@ def test_binding_refuses_host_tensors(hiplib):
     with pytest.raises(ValueError):  # key rows must be [num_seqs, num_kv_heads, head_dim]
         hiplib.reshape_and_decode(torch.empty_like(q), q, x[:1], x[:1], kc, kc, sl, bt, cl, 0.1, 16,
                                   partition_size=0)
+
+
+def _step_ok_brute(slots, bt, cl, num_blocks, bs):
+    """Plain definition of pa_validate_step_host's condition, slot by slot."""
+    B, M = bt.shape
+    for s in range(B):
+        L = int(cl[s])
+        if L < 0 or (L + bs - 1) // bs > M:
+            return False
+        for j in range((L + bs - 1) // bs):
+            if not 0 <= bt[s, j] < num_blocks:
+                return False
+    live = [int(x) for x in slots if x >= 0]
+    if any(x >= num_blocks * bs for x in live) or len(set(live)) != len(live):
+        return False
+    for s in range(B):
+        slot = int(slots[s])
+        if slot < 0:
+            continue
+        for r in range(B):                       # every position every context reads
+            for t in range(int(cl[r])):
+                pos_slot = int(bt[r, t // bs]) * bs + t % bs
+                if pos_slot == slot and not (r == s and t == int(cl[s]) - 1):
+                    return False
+    return True
+
+
+def test_step_validator_matches_brute_force(hiplib):
+    rng = np.random.default_rng(31)
+    agree = {True: 0, False: 0}
+    for _ in range(300):
+        bs = int(rng.choice([8, 16, 32]))
+        B, M, N = int(rng.integers(1, 5)), int(rng.integers(1, 4)), int(rng.integers(2, 9))
+        bt = rng.integers(0, N, size=(B, M)).astype(np.int32)   # blocks may be shared
+        cl = rng.integers(0, M * bs + 1, size=B).astype(np.int32)
+        slots = np.full(B, -1, np.int64)
+        for s in range(B):
+            r = rng.random()
+            if r < 0.5 and cl[s] > 0:            # its own last position
+                t = int(cl[s]) - 1
+                slots[s] = int(bt[s, t // bs]) * bs + t % bs
+            elif r < 0.85:                       # anywhere in the pool
+                slots[s] = int(rng.integers(0, N * bs))
+        want = _step_ok_brute(slots, bt, cl, N, bs)
+        got = hiplib.validate_step_host(slots, bt, cl, N, bs)
+        assert (got == OK) == want, (bt, cl, slots, bs, got)
+        agree[want] += 1
+    assert agree[True] > 20 and agree[False] > 20   # both outcomes exercised
