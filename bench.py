@@ -48,6 +48,9 @@ def parse_args(argv=None):
     ap.add_argument("--two-call", action="store_true",
                     help="step = pa_reshape_and_cache then pa_paged_attention_decode (default: "
                          "pa_reshape_and_decode, the KV write inside the decode launch)")
+    ap.add_argument("--read-ceiling", action="store_true",
+                    help="also time plain streaming HBM traffic for context: a sum over 4 GiB "
+                         "(reads) and a 2 GiB device copy (reads + writes), torch kernels")
     ap.add_argument("--decode-only", action="store_true",
                     help="time only the decode call per step (profiling aid)")
     ap.add_argument("--pool-copies", type=int, default=2,
@@ -158,6 +161,40 @@ def _cpu_model() -> str:
     except OSError:
         pass
     return "unknown"
+
+
+def read_ceiling(dev):
+    """Plain streaming HBM rates on this GPU for context next to the 8 TB/s
+    nominal peak: torch's sum over a 4 GiB fp16 tensor (reads) and a 2 GiB
+    device-to-device copy (reads + writes), each the median of 10 timed
+    calls with HIP events."""
+    import numpy as np
+    import torch
+    x = torch.ones(2 << 30, dtype=torch.float16, device=dev)       # 4 GiB
+    y = torch.empty(1 << 30, dtype=torch.float16, device=dev)      # 2 GiB
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        ts = []
+        for _ in range(10):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        return float(np.median(ts)) * 1e-3
+
+    t_sum = timed(lambda: x.sum(dtype=torch.float32))
+    t_copy = timed(lambda: y.copy_(x[: 1 << 30]))
+    out = {"sum_4GiB_read_GBps": round(x.numel() * 2 / t_sum / 1e9, 1),
+           "copy_2GiB_read_write_GBps": round(2 * y.numel() * 2 / t_copy / 1e9, 1),
+           "note": "torch kernels, median of 10; nominal HBM peak 8000 GB/s"}
+    del x, y
+    torch.cuda.empty_cache()
+    return out
 
 
 def decode_loop(args, w, dev):
@@ -578,6 +615,8 @@ def main(argv=None) -> int:
         result["multi_query"] = multi_query_bench(args, w, d, pools, part, stream)
     if args.block_ops:
         result["block_ops"] = block_ops(w, dev)
+    if args.read_ceiling:
+        result["read_ceiling"] = read_ceiling(dev)
     if args.loop_steps > 0:
         del pools, d, ws
         torch.cuda.empty_cache()
