@@ -324,7 +324,9 @@ __device__ __forceinline__ void wait_lds_loads() { asm volatile("s_waitcnt vmcnt
 // as 16x16x32 products.  No branch separates the row
 // tiles, so their matrix-core chains interleave.  MASKED: a token counts for
 // row n when it is one of its tile's valid tokens and not past the row's
-// position pos_n; rows that see none of the group add nothing.
+// position pos_n; rows that see none of the group add nothing.  Scores stay
+// raw until the exponent (one fma per score: scale * s - max); scale_log2
+// must be >= 0 (the caller turns a negative scale into a negated query).
 template <int DT, int D, int NT, int RT, bool MASKED, typename Tile>
 __device__ __forceinline__ void fold_group(MfmaState<D> (&st)[RT],
                                            const u32x4 (&qb)[RT][D / 32],
@@ -350,7 +352,7 @@ __device__ __forceinline__ void fold_group(MfmaState<D> (&st)[RT],
     for (int r = 0; r < RT; ++r)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        sc[r][t][e] = sacc[r][e] * scale_log2;
+        sc[r][t][e] = sacc[r][e];  // raw; the scale goes into the exponent's fma
         if constexpr (MASKED) {
           const int k = ln.g + 4 * e;
           const bool ok = k < lims[t] && g_first + kBlockSize * t + k <= pos_n[r];
@@ -371,7 +373,9 @@ __device__ __forceinline__ void fold_group(MfmaState<D> (&st)[RT],
   }
 #pragma unroll
   for (int r = 0; r < RT; ++r) {
-    mb[r] = xor32_combine(mb[r], MaxOp{});
+    // the largest raw score, scaled (scale_log2 >= 0 keeps it the largest)
+    const float mr = xor32_combine(mb[r], MaxOp{});
+    mb[r] = mr == -INFINITY ? -INFINITY : mr * scale_log2;
     grow = grow || mb[r] > st[r].m + kRescaleSlack;
   }
   if (__builtin_amdgcn_ballot_w64(grow) != 0) {  // wave-uniform; a rescale to a larger max
@@ -402,8 +406,10 @@ __device__ __forceinline__ void fold_group(MfmaState<D> (&st)[RT],
       float p[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        p[e] = fast_exp2(sc[r][t][e] - st[r].m);
-        if constexpr (MASKED) p[e] = none ? 0.f : p[e];
+        p[e] = fast_exp2(__builtin_fmaf(sc[r][t][e], scale_log2, -st[r].m));
+        // dropped tokens (and rows with none so far) weigh nothing, also when
+        // the scale is 0 (-inf * 0 is not -inf)
+        if constexpr (MASKED) p[e] = (none || sc[r][t][e] == -INFINITY) ? 0.f : p[e];
       }
       sum += (p[0] + p[1]) + (p[2] + p[3]);
       pa[r][t] = u32x2{pack2<DT>(p[0], p[1]), pack2<DT>(p[2], p[3])};
@@ -512,6 +518,16 @@ __global__ __launch_bounds__(NW * 64, 2) void multi_query_wide_kernel(MultiQuery
       qb[r][jj] = active ? q[qrow * S::CPR + 4 * jj + ln.g] : u32x4{0u, 0u, 0u, 0u};
     st[r].reset();
   });
+  // fold_group takes a non-negative scale: scale * (q.k) = |scale| * ((-q).k),
+  // and flipping the sign bits of the 16-bit q elements negates q exactly.
+  const float sl = __builtin_fabsf(a.scale_log2);
+  if (a.scale_log2 < 0.f) {
+    static_for<0, RT>([&](auto rc) __attribute__((always_inline)) {
+      constexpr int r = decltype(rc)::value;
+#pragma unroll
+      for (int jj = 0; jj < S::NJ; ++jj) qb[r][jj] ^= u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+    });
+  }
 
   const int32_t* __restrict__ bt = a.block_tables + (int64_t)s * a.max_blocks_per_seq;
   const int jb = part * a.part_blocks;
@@ -586,10 +602,10 @@ __global__ __launch_bounds__(NW * 64, 2) void multi_query_wide_kernel(MultiQuery
           const int(&lh)[FT] = *reinterpret_cast<const int(*)[FT]>(&lims[t0]);
           if (whole)
             fold_group<DT, D, FT, RT, false>(st, qb, pos_n, &sm.t[b][t0], lh,
-                                                     g_first + t0 * kBlockSize, a.scale_log2, ln);
+                                                     g_first + t0 * kBlockSize, sl, ln);
           else
             fold_group<DT, D, FT, RT, true>(st, qb, pos_n, &sm.t[b][t0], lh,
-                                                    g_first + t0 * kBlockSize, a.scale_log2, ln);
+                                                    g_first + t0 * kBlockSize, sl, ln);
         });
       }
       wait_lds_loads();

@@ -154,3 +154,22 @@ def test_full_shapes_sampled(cuda, name, qlen, part):
     ref = oracle_mq(w, spans, (toks, heads))
     check_close(to_f64(got_raw[toks, heads], w.dtype), ref, w.dtype, f"{name} q{qlen}")
     assert not np.isnan(to_f64(got_raw, w.dtype)).any()
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.09, 0.15])
+def test_scale_sign_and_zero(cuda, scale):
+    """Zero, negative and large scales on wide items (the scale is folded into
+    the exponent; a negative one becomes a negated query) and on
+    tile-splitting items, against the oracle.  (At scale 0.3 the softmax is
+    so peaked that the bf16 weights of the P.V products alone put the
+    max-abs error at 0.015, above the bf16 bound, in this kernel and the one
+    before the scale moved into the exponent alike.)"""
+    announce("multi-query scale", scale)
+    lens, nqs = [300, 128, 70, 45], [16, 8, 12, 3]
+    for G, part in ((8, 0), (8, 64), (2, 0)):
+        w, run = prepared(cuda, dtype="bf16", head_dim=128, num_kv_heads=2, num_q_heads=2 * G,
+                          lens=lens, seed=97, scale=scale)
+        spans = W.generate_query_spans(w, nqs, seed=96)
+        ref = oracle_mq(w, spans)
+        got = to_f64(run_mq(run, spans, cuda, part), "bf16")
+        check_close(got, ref, "bf16", f"scale {scale} G{G} partition {part}")
