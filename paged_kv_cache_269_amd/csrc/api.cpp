@@ -10,6 +10,7 @@
 #include <utility>
 #include <vector>
 
+#include "items.h"
 #include "launch.h"
 
 namespace {
@@ -150,6 +151,12 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   a.scale_log2 = scale * 1.4426950408889634f;
   a.block_size = block_size;
   a.num_blocks = num_blocks;
+  {
+    // every item starts at once when there are no more than compute units
+    const int cus = pa::compute_units();
+    const int64_t items = (int64_t)num_seqs * num_q_heads * parts;
+    a.grid_order = (cus > 0 && items <= cus) ? 1 : 0;
+  }
 
   const hipStream_t st = (hipStream_t)stream;
   const int group = num_q_heads / num_kv_heads;

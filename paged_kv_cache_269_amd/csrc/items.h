@@ -149,11 +149,13 @@ __device__ __forceinline__ void store_row_part(const void* cache, int64_t off, c
 // (longest-processing-time-first list scheduling).  Each wave finds its
 // sequence by bisection on the length, counting with ballots over the
 // lengths held in registers.  Launches with more than kOrderMaxSeqs
-// sequences keep the grid order.
+// sequences keep the grid order, and so do launches whose items all start at
+// once (no more items than compute units: the order cannot matter there, and
+// skipping it saves each item the loads it needs).
 constexpr int kOrderMaxSeqs = 256;
 
 __device__ __forceinline__ int longest_first(const DecodeArgs& a, int slot) {
-  if (a.num_seqs > kOrderMaxSeqs) return slot;
+  if (a.num_seqs > kOrderMaxSeqs || a.grid_order) return slot;
   const int lane = threadIdx.x & 63;
   constexpr int kChunks = kOrderMaxSeqs / 64;
   int len[kChunks];

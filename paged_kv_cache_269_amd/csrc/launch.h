@@ -44,6 +44,8 @@ struct DecodeArgs {
   const void* new_v;
   const int64_t* new_slots;     // [B]
   int64_t num_blocks;           // N (slot bound of the write)
+  int grid_order;               // 1: grid slots take the sequences in grid order (a launch
+                                // whose items all start at once; see longest_first)
 };
 
 // Outputs of the shared-prefix kernel (the same arrays DecodeArgs reads).
