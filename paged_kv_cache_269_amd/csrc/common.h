@@ -14,9 +14,6 @@ enum Dtype : int { kF32 = 0, kF16 = 1, kBF16 = 2 };
 constexpr int kBlockSize = 16;   // tokens per tile the kernels work on (= pool block by default)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-// Online softmax: how far (base 2) a score may pass the running max before
-// the max, and with it the accumulators' scale, is moved.
-constexpr float kRescaleSlack = 8.f;
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));

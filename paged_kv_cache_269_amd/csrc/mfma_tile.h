@@ -63,6 +63,17 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
   return (uint32_t)to_bits16<DT>(lo) | ((uint32_t)to_bits16<DT>(hi) << 16);
 }
 
+// Sum of the four 16-bit weights of a packed P operand, exactly the values
+// the matrix core multiplies with.
+template <int DT>
+__device__ __forceinline__ float packed_sum(const u32x2& w) {
+  const uint32_t w0 = w[0], w1 = w[1];
+  float a, b, c, d;
+  unpack2<DT>(w0, a, b);
+  unpack2<DT>(w1, c, d);
+  return (a + b) + (c + d);
+}
+
 // 16-bit element k of a row slice held as EPL elements.
 template <int EPL>
 struct VSlice;
@@ -250,11 +261,10 @@ __device__ __forceinline__ void fold_tile(MfmaState<D>& st, const u32x4 (&qb)[D 
   float mb = __builtin_fmaxf(__builtin_fmaxf(sc[0], sc[1]), __builtin_fmaxf(sc[2], sc[3]));
   mb = xor16_combine(mb, MaxOp{});
   mb = xor32_combine(mb, MaxOp{});
-  // The running max moves only when a score passes it by more than
-  // kRescaleSlack: until then the tile's weights are taken against the older
-  // max (each below 2^kRescaleSlack) and the accumulators keep their scale.
-  // Numerator and denominator share that max, so the result is unchanged.
-  if (__builtin_amdgcn_ballot_w64(mb > st.m + kRescaleSlack) != 0) {  // wave-uniform
+  // The running max follows every rise, so every weight is at most 1 and the
+  // largest weight of a peaked row is exactly 1 (no rounding error in its
+  // 16-bit P operand).  The test is wave-uniform: any row's rise rescales all.
+  if (__builtin_amdgcn_ballot_w64(mb > st.m) != 0) {
     const float mn = __builtin_fmaxf(st.m, mb);
     const float alpha = mn == -INFINITY ? 1.f : fast_exp2(st.m - mn);
     st.lsum *= alpha;
@@ -278,8 +288,10 @@ __device__ __forceinline__ void fold_tile(MfmaState<D>& st, const u32x4 (&qb)[D 
       for (int e = 0; e < 4; ++e) p[e] = 0.f;
     }
   }
-  st.lsum += (p[0] + p[1]) + (p[2] + p[3]);
   const u32x2 pa{pack2<DT>(p[0], p[1]), pack2<DT>(p[2], p[3])};
+  // The normaliser sums the weights as rounded for P.V, so numerator and
+  // denominator weigh every token alike.
+  st.lsum += packed_sum<DT>(pa);
 #pragma unroll
   for (int jj = 0; jj < S::EPL; ++jj) st.o[jj] = mfma_pv<DT>(pa, vb[jj], st.o[jj]);
 }

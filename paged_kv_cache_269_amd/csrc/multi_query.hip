@@ -376,11 +376,14 @@ __device__ __forceinline__ void fold_group(MfmaState<D> (&st)[RT],
     // the largest raw score, scaled (scale_log2 >= 0 keeps it the largest)
     const float mr = xor32_combine(mb[r], MaxOp{});
     mb[r] = mr == -INFINITY ? -INFINITY : mr * scale_log2;
-    grow = grow || mb[r] > st[r].m + kRescaleSlack;
+    grow = grow || mb[r] > st[r].m;
   }
-  if (__builtin_amdgcn_ballot_w64(grow) != 0) {  // wave-uniform; a rescale to a larger max
-#pragma unroll                                   // never changes the result, so all row
-    for (int r = 0; r < RT; ++r) {               // tiles take it
+  // The running max follows every rise (weights at most 1, a peaked row's
+  // largest weight exactly 1).  Wave-uniform: a rescale to a larger max
+  // never changes the result, so all row tiles take it.
+  if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
       const float mn = __builtin_fmaxf(st[r].m, mb[r]);
       const float alpha = mn == -INFINITY ? 1.f : fast_exp2(st[r].m - mn);
       st[r].lsum *= alpha;
@@ -411,8 +414,8 @@ __device__ __forceinline__ void fold_group(MfmaState<D> (&st)[RT],
         // the scale is 0 (-inf * 0 is not -inf)
         if constexpr (MASKED) p[e] = (none || sc[r][t][e] == -INFINITY) ? 0.f : p[e];
       }
-      sum += (p[0] + p[1]) + (p[2] + p[3]);
       pa[r][t] = u32x2{pack2<DT>(p[0], p[1]), pack2<DT>(p[2], p[3])};
+      sum += packed_sum<DT>(pa[r][t]);  // the weights as rounded for P.V
     }
     st[r].lsum += sum;
   }
