@@ -78,3 +78,10 @@ def oracle_rows(w: W.Workload, seqs, heads):
     out, _, _ = oracle.decode_rows(w.q, w.k_cache, w.v_cache, w.block_tables, w.context_lens,
                                    w.scale, w.dtype, seqs, heads)
     return out
+
+
+def oracle_all(w: W.Workload) -> np.ndarray:
+    """Every output row [B, Hq, D] of the workload (its pools as they stand),
+    on all host threads."""
+    return oracle.decode(w.q, w.k_cache, w.v_cache, w.block_tables, w.context_lens, w.scale,
+                         w.dtype)

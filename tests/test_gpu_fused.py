@@ -19,7 +19,7 @@ import torch
 import oracle
 from paged_kv_cache_269_amd import workloads as W
 
-from parity import Run, check_close, oracle_rows, tensor_to_np, to_f64
+from parity import Run, check_close, oracle_all, oracle_rows, tensor_to_np, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -136,7 +136,7 @@ def test_fused_block_sizes(cuda, bs, dtype, G):
 def test_fused_full_size(cuda, name):
     """The full workload in the benchmark's launch configuration (its own
     partition size): pool after the call equal to the two-call form's, output
-    bit-identical to it, and sampled rows against the oracle."""
+    bit-identical to it, and every row against the oracle."""
     announce("fused full", name)
     w = W.generate(name)
     run = Run(w, cuda)
@@ -150,13 +150,8 @@ def test_fused_full_size(cuda, name):
     for a, b in zip(pool_bits(run, w), pool_bits(base_run, w)):
         assert np.array_equal(a, b)
     w2 = after_write(w)
-    rng = np.random.default_rng(5)
-    B, Hq = w.num_seqs, w.num_q_heads
-    flat = rng.choice(B * Hq, size=min(48, B * Hq), replace=False)
-    seqs, heads = flat // Hq, flat % Hq
-    ref = oracle_rows(w2, seqs, heads)
-    got = to_f64(tensor_to_np(out, w.dtype)[seqs, heads], w.dtype)
-    announce(name, check_close(got, ref, w.dtype, f"{name} fused full size"))
+    got = to_f64(tensor_to_np(out, w.dtype), w.dtype)
+    announce(name, check_close(got, oracle_all(w2), w.dtype, f"{name} fused full size"))
 
 
 def test_fused_slots_elsewhere(cuda):
@@ -229,7 +224,7 @@ def test_fused_cascade(cuda, case):
     """pa_reshape_and_decode_cascade on shared-prefix batches (new-token slots
     hold NaN before the call): pool equal to the oracle's write, output
     bit-identical to the KV-write kernel + cascade call and within tolerance
-    of the oracle (all rows, or a sample at full size)."""
+    of the oracle (every row)."""
     import paged_kv_cache_269_amd as pa
     name, over = case
     announce("fused cascade", name, over)
@@ -246,16 +241,7 @@ def test_fused_cascade(cuda, case):
     w2 = after_write(w)
     kc, vc = pool_bits(run, w)
     assert np.array_equal(kc, w2.k_cache.view(view)) and np.array_equal(vc, w2.v_cache.view(view))
-    B, Hq = w.num_seqs, w.num_q_heads
-    if B * Hq <= 1024:
-        ref = full_oracle(w2)
-        stats = check_close(to_f64(got_raw, w.dtype), ref, w.dtype, f"cascade {over}")
-    else:
-        rng = np.random.default_rng(9)
-        flat = rng.choice(B * Hq, size=64, replace=False)
-        seqs, heads = flat // Hq, flat % Hq
-        stats = check_close(to_f64(got_raw[seqs, heads], w.dtype), oracle_rows(w2, seqs, heads),
-                            w.dtype, "cascade full size")
+    stats = check_close(to_f64(got_raw, w.dtype), oracle_all(w2), w.dtype, f"cascade {over}")
     announce(stats)
 
 
