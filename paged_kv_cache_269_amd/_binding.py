@@ -141,6 +141,19 @@ def _stream_handle(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _on_stream(stream, alloc):
+    """Run ``alloc`` (a workspace allocation the caller left to the wrapper)
+    with ``stream`` current.  torch's caching allocator hands a freed block
+    only to later work of the stream it was allocated on, so the workspace,
+    dropped when the wrapper returns, is not reused while this call's
+    kernels on ``stream`` may still write it."""
+    import torch
+    if stream is None:
+        return alloc()
+    with torch.cuda.stream(stream):
+        return alloc()
+
+
 def reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, stream=None) -> None:
     """k_cache[slot // 16, h, slot % 16, :] = key[i, h, :] (and V) for slot >= 0."""
     import torch
@@ -190,7 +203,8 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
     if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.shape != (B,):
         raise ValueError("block_tables must be [num_seqs, max_blocks], context_lens [num_seqs]")
     if workspace is None:
-        workspace = decode_workspace(B, Hq, D, max_context_len, partition_size, q.device)
+        workspace = _on_stream(stream, lambda: decode_workspace(
+            B, Hq, D, max_context_len, partition_size, q.device))
     ws_ptr = _dev_ptr(workspace, "workspace") if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     rc = load_library().pa_paged_attention_decode(
@@ -222,7 +236,8 @@ def reshape_and_decode(out, q, key, value, k_cache, v_cache, slot_mapping, block
     if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.shape != (B,):
         raise ValueError("block_tables must be [num_seqs, max_blocks], context_lens [num_seqs]")
     if workspace is None:
-        workspace = decode_workspace(B, Hq, D, max_context_len, partition_size, q.device)
+        workspace = _on_stream(stream, lambda: decode_workspace(
+            B, Hq, D, max_context_len, partition_size, q.device))
     ws_ptr = _dev_ptr(workspace, "workspace") if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     rc = load_library().pa_reshape_and_decode(
@@ -264,7 +279,7 @@ def paged_attention_decode_cascade(out, q, k_cache, v_cache, block_tables, conte
     if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.shape != (B,):
         raise ValueError("block_tables must be [num_seqs, max_blocks], context_lens [num_seqs]")
     if workspace is None:
-        workspace = cascade_workspace(B, Hq, D, q.device)
+        workspace = _on_stream(stream, lambda: cascade_workspace(B, Hq, D, q.device))
     rc = load_library().pa_paged_attention_decode_cascade(
         _dev_ptr(out, "out"), _dev_ptr(q, "q"), _dev_ptr(k_cache, "k_cache"),
         _dev_ptr(v_cache, "v_cache"), _dev_ptr(block_tables, "block_tables", torch.int32),
@@ -294,7 +309,7 @@ def reshape_and_decode_cascade(out, q, key, value, k_cache, v_cache, slot_mappin
     if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.shape != (B,):
         raise ValueError("block_tables must be [num_seqs, max_blocks], context_lens [num_seqs]")
     if workspace is None:
-        workspace = cascade_workspace(B, Hq, D, q.device)
+        workspace = _on_stream(stream, lambda: cascade_workspace(B, Hq, D, q.device))
     rc = load_library().pa_reshape_and_decode_cascade(
         _dev_ptr(out, "out"), _dev_ptr(q, "q"), _dev_ptr(key, "key"), _dev_ptr(value, "value"),
         _dev_ptr(k_cache, "k_cache"), _dev_ptr(v_cache, "v_cache"),
@@ -345,7 +360,8 @@ def paged_attention_multi_query(out, q, k_cache, v_cache, block_tables, context_
     if query_start.shape != (B + 1,):
         raise ValueError("query_start must be [num_seqs + 1]")
     if workspace is None:
-        workspace = multi_query_workspace(T, Hq, D, max_context_len, partition_size, q.device)
+        workspace = _on_stream(stream, lambda: multi_query_workspace(
+            T, Hq, D, max_context_len, partition_size, q.device))
     ws_ptr = _dev_ptr(workspace, "workspace") if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     rc = load_library().pa_paged_attention_multi_query(
