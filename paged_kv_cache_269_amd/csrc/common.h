@@ -14,6 +14,16 @@ enum Dtype : int { kF32 = 0, kF16 = 1, kBF16 = 2 };
 constexpr int kBlockSize = 16;   // tokens per tile the kernels work on (= pool block by default)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+// Online softmax of the matrix-core folds: how far (base 2) a tile's max may
+// pass the running max before the running max -- and with it the
+// accumulators' scale -- moves.  Weights then stay below 2^slack before
+// they are rounded to the 16-bit P operand; a slack of 1 rescales far less
+// often than 0 (every rise) with the same accuracy once the normaliser sums
+// the rounded weights (CPU emulation of the fold over seeded peaked rows).
+#ifndef PA_RESCALE_SLACK
+#define PA_RESCALE_SLACK 1
+#endif
+constexpr float kRescaleSlack = PA_RESCALE_SLACK;
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));

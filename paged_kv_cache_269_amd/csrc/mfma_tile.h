@@ -261,10 +261,10 @@ __device__ __forceinline__ void fold_tile(MfmaState<D>& st, const u32x4 (&qb)[D 
   float mb = __builtin_fmaxf(__builtin_fmaxf(sc[0], sc[1]), __builtin_fmaxf(sc[2], sc[3]));
   mb = xor16_combine(mb, MaxOp{});
   mb = xor32_combine(mb, MaxOp{});
-  // The running max follows every rise, so every weight is at most 1 and the
-  // largest weight of a peaked row is exactly 1 (no rounding error in its
-  // 16-bit P operand).  The test is wave-uniform: any row's rise rescales all.
-  if (__builtin_amdgcn_ballot_w64(mb > st.m) != 0) {
+  // The running max moves once a score passes it by more than kRescaleSlack,
+  // so every weight stays below 2^kRescaleSlack.  The test is wave-uniform:
+  // any row's rise rescales all.
+  if (__builtin_amdgcn_ballot_w64(mb > st.m + kRescaleSlack) != 0) {
     const float mn = __builtin_fmaxf(st.m, mb);
     const float alpha = mn == -INFINITY ? 1.f : fast_exp2(st.m - mn);
     st.lsum *= alpha;

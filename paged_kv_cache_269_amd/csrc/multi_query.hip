@@ -376,10 +376,11 @@ __device__ __forceinline__ void fold_group(MfmaState<D> (&st)[RT],
     // the largest raw score, scaled (scale_log2 >= 0 keeps it the largest)
     const float mr = xor32_combine(mb[r], MaxOp{});
     mb[r] = mr == -INFINITY ? -INFINITY : mr * scale_log2;
-    grow = grow || mb[r] > st[r].m;
+    grow = grow || mb[r] > st[r].m + kRescaleSlack;
   }
-  // The running max follows every rise (weights at most 1, a peaked row's
-  // largest weight exactly 1).  Wave-uniform: a rescale to a larger max
+  // The running max moves once a score passes it by more than
+  // kRescaleSlack (weights stay below 2^kRescaleSlack).  Wave-uniform: a
+  // rescale to a larger max
   // never changes the result, so all row tiles take it.
   if (__builtin_amdgcn_ballot_w64(grow) != 0) {
 #pragma unroll
