@@ -72,7 +72,9 @@ enum pa_status {
                              (pa_cascade_workspace_bytes for the cascade entry point) */
   PA_ERR_RANGE = 5,       /* host table check: an entry, length or slot out of range */
   PA_ERR_LAUNCH = 6,      /* the HIP runtime refused a launch */
-  PA_ERR_EXHAUSTED = 7    /* block manager (pagedattn_blocks.h): no free block left */
+  PA_ERR_EXHAUSTED = 7,   /* block manager (pagedattn_blocks.h): no free block left */
+  PA_ERR_SCRATCH = 8      /* pa_reshape_and_decode_static: the partials need more than
+                             PA_STATIC_SCRATCH_BYTES */
 };
 
 /*
@@ -158,6 +160,36 @@ int pa_reshape_and_decode(void* out, const void* q, const void* key, const void*
                           int64_t num_blocks, float scale, int32_t dtype, int32_t partition_size,
                           int32_t max_context_len, void* workspace, size_t workspace_bytes,
                           void* stream);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the step
+ * of pa_reshape_and_decode with no workspace argument.  Its split-K partials
+ * live in a device array the library owns, PA_STATIC_SCRATCH_BYTES
+ * (64 MiB) per GPU, held from the library's load until the process ends.
+ * Same arguments (minus workspace), result, precondition and errors as
+ * pa_reshape_and_decode, plus PA_ERR_SCRATCH when the launch's partials
+ * (pa_decode_workspace_bytes of its sizes) exceed the array, and
+ * PA_ERR_LAUNCH when the array's address cannot be found on the current
+ * device.  It calls no allocating routine; the array's device address is
+ * looked up once per device, on the first call made with that device
+ * current.
+ *
+ * Unlike every other call this one keeps state: all calls on one GPU share
+ * its array, which holds the last call's partials afterwards (no call reads
+ * what an earlier one left: every slot the merge reads is written first in
+ * the same call).  Calls that overlap on one GPU -- enqueued on different
+ * streams without ordering between them -- race on the array and give
+ * undefined results; calls on one stream, or ordered by events, are safe.
+ */
+#define PA_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+int pa_reshape_and_decode_static(void* out, const void* q, const void* key, const void* value,
+                                 void* k_cache, void* v_cache, const int64_t* slot_mapping,
+                                 const int32_t* block_tables, const int32_t* context_lens,
+                                 int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                                 int64_t num_blocks, float scale, int32_t dtype,
+                                 int32_t partition_size, int32_t max_context_len, void* stream);
 
 /*
  * Split-K merge.  Sequence s has P = ceil(L / partition_size) partitions,

@@ -26,6 +26,8 @@ from ._binding import (  # noqa: F401
     reshape_and_cache,
     reshape_and_decode,
     reshape_and_decode_cascade,
+    reshape_and_decode_static,
+    STATIC_SCRATCH_BYTES,
     status_string,
     swap_blocks,
     swap_blocks_mapped,
@@ -44,7 +46,7 @@ __all__ = [
     "lib_path", "load_library", "multi_query_workspace", "multi_query_workspace_bytes",
     "paged_attention_decode", "paged_attention_decode_cascade", "paged_attention_multi_query",
     "paged_attention_reduce", "reshape_and_cache", "reshape_and_decode", "reshape_and_decode_cascade",
-    "status_string",
+    "reshape_and_decode_static", "STATIC_SCRATCH_BYTES", "status_string",
     "swap_blocks",
     "swap_blocks_mapped",
     "validate_copy_host", "validate_query_start_host", "validate_slots_host", "validate_step_host",

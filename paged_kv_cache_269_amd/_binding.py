@@ -19,6 +19,9 @@ _LIB_PATH = os.environ.get("PAGEDATTN_LIB") or os.path.join(_HERE, "libpagedattn
 
 PA_OK, PA_ERR_NULL, PA_ERR_SHAPE, PA_ERR_UNSUPPORTED = 0, 1, 2, 3
 PA_ERR_WORKSPACE, PA_ERR_RANGE, PA_ERR_LAUNCH, PA_ERR_EXHAUSTED = 4, 5, 6, 7
+PA_ERR_SCRATCH = 8
+# Size of the library's static scratch array (PA_STATIC_SCRATCH_BYTES).
+STATIC_SCRATCH_BYTES = 64 << 20
 
 # Every symbol the header declares, with its ctypes signature.
 _P, _I32, _I64, _F32, _SZ = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
@@ -36,6 +39,9 @@ EXPORTS = {
     "pa_reshape_and_decode": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32,
                                              _I32, _I32, _I32, _I32, _I64, _F32, _I32, _I32,
                                              _I32, _P, _SZ, _P]),
+    "pa_reshape_and_decode_static": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I32,
+                                                    _I32, _I32, _I32, _I32, _I32, _I64, _F32,
+                                                    _I32, _I32, _I32, _P]),
     "pa_paged_attention_reduce": (ctypes.c_int, [_P, _P, _P, _P, _P, _I32, _I32, _I32, _I32,
                                                  _I32, _I32, _P]),
     "pa_decode_workspace_bytes": (ctypes.c_size_t, [_I32, _I32, _I32, _I32, _I32]),
@@ -249,6 +255,35 @@ def reshape_and_decode(out, q, key, value, k_cache, v_cache, slot_mapping, block
         block_tables.shape[1], N, float(scale), _dtype_code(q), int(partition_size),
         int(max_context_len), ws_ptr, ws_bytes, _stream_handle(stream))
     _check("pa_reshape_and_decode", rc)
+
+
+def reshape_and_decode_static(out, q, key, value, k_cache, v_cache, slot_mapping, block_tables,
+                              context_lens, scale: float, max_context_len: int,
+                              partition_size: int = 512, stream=None) -> None:
+    """reshape_and_decode with its partials in the library's static device
+    array (pa_reshape_and_decode_static): no workspace, no allocation.  All
+    calls on one GPU share the array; calls that overlap on one GPU race."""
+    import torch
+    B, Hq, D = q.shape
+    N, Hkv, bs, D2 = k_cache.shape
+    if out.shape != q.shape or D2 != D or v_cache.shape != k_cache.shape:
+        raise ValueError("shape mismatch between q, out and the caches")
+    if key.shape != (B, Hkv, D) or value.shape != key.shape or slot_mapping.shape != (B,):
+        raise ValueError("key/value must be [num_seqs, num_kv_heads, head_dim], "
+                         "slot_mapping [num_seqs]")
+    if not (q.dtype == out.dtype == key.dtype == value.dtype == k_cache.dtype == v_cache.dtype):
+        raise TypeError("q, out, key, value and caches must share one element type")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.shape != (B,):
+        raise ValueError("block_tables must be [num_seqs, max_blocks], context_lens [num_seqs]")
+    rc = load_library().pa_reshape_and_decode_static(
+        _dev_ptr(out, "out"), _dev_ptr(q, "q"), _dev_ptr(key, "key"), _dev_ptr(value, "value"),
+        _dev_ptr(k_cache, "k_cache"), _dev_ptr(v_cache, "v_cache"),
+        _dev_ptr(slot_mapping, "slot_mapping", torch.int64),
+        _dev_ptr(block_tables, "block_tables", torch.int32),
+        _dev_ptr(context_lens, "context_lens", torch.int32), B, Hq, Hkv, D, bs,
+        block_tables.shape[1], N, float(scale), _dtype_code(q), int(partition_size),
+        int(max_context_len), _stream_handle(stream))
+    _check("pa_reshape_and_decode_static", rc)
 
 
 def cascade_workspace_bytes(num_seqs: int, num_q_heads: int, head_dim: int) -> int:

@@ -15,7 +15,7 @@ ARCH = "gfx950"
 
 SOURCES = ["api.cpp", "api_blocks.cpp", "block_manager.cpp", "reshape_and_cache.hip", "copy_blocks.hip",
            "decode_valu.hip", "decode_mfma.hip", "prefix.hip", "multi_query.hip",
-           "reduce.hip"]
+           "reduce.hip", "decode_static.hip"]
 
 # Packed fp32 ALU ops are kept out of the generated code.  Matrix-core
 # accumulators are kept in ordinary VGPRs: the online-softmax rescale works on

@@ -232,6 +232,8 @@ const char* pa_status_string(int status) {
     case PA_ERR_RANGE: return "table entry, context length or slot out of range";
     case PA_ERR_LAUNCH: return "the HIP runtime refused a kernel launch";
     case PA_ERR_EXHAUSTED: return "KV cache exhausted: no free block left";
+    case PA_ERR_SCRATCH:
+      return "the partials need more than the library's static scratch array holds";
     default: return "unknown status";
   }
 }

@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol(hiplib):
 
 def test_version_and_status_strings(hiplib):
     assert "gfx950" in hiplib.version()
-    for code in range(0, 8):
+    for code in range(0, 9):
         assert hiplib.status_string(code) and hiplib.status_string(code) != "unknown status"
     assert hiplib.status_string(99) == "unknown status"
 
