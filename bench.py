@@ -66,6 +66,11 @@ def parse_args(argv=None):
     ap.add_argument("--query-len", type=int, default=0,
                     help="also time pa_paged_attention_multi_query with this many new query "
                          "tokens per sequence (causal over each context's last tokens)")
+    ap.add_argument("--no-config-rows", action="store_true",
+                    help="skip the per-workload rows (by default every workload of the five "
+                         "is also timed for a few steps and checked against the oracle)")
+    ap.add_argument("--row-steps", type=int, default=20,
+                    help="timed steps of each per-workload row")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB before warmup, as the "
                          "known-size reference for HBM byte counters")
@@ -82,13 +87,17 @@ def _code_only(text: str) -> str:
 
 def kernel_source_hash() -> str:
     """Hash of the decode kernel sources' code (comments and layout
-    ignored), to tell whether stored counters still describe the code being
-    run."""
+    ignored) and of the compiler flags they are built with, to tell whether
+    stored counters still describe the code being run."""
+    from paged_kv_cache_269_amd import build as hipbuild
     h = hashlib.sha256()
     for f in ("common.h", "items.h", "launch.h", "mfma_tile.h", "decode_valu.hip",
               "decode_mfma.hip", "prefix.hip", "reduce.hip", "reshape_and_cache.hip", "api.cpp"):
         with open(os.path.join(ROOT, "paged_kv_cache_269_amd", "csrc", f)) as fh:
             h.update(_code_only(fh.read()).encode())
+    # flags with the checkout's own path taken out (it differs between machines)
+    flags = [f.replace(ROOT, "<root>") for f in hipbuild.COMMON_FLAGS]
+    h.update(" ".join([hipbuild.HIPCC.rsplit("/", 1)[-1], hipbuild.ARCH] + flags).encode())
     return h.hexdigest()[:16]
 
 
@@ -434,27 +443,23 @@ def multi_query_bench(args, w, d, pools, part, stream):
             "tokens_per_s": round(T / us * 1e6, 1)}
 
 
-def main(argv=None) -> int:
-    args = parse_args(argv)
-    if args.gpus != 1:
-        print(json.dumps({"error": "this benchmark runs on exactly one GPU; "
-                                   f"--gpus {args.gpus} is not supported (no multi-GPU path "
-                                   "in this build)"}))
-        return 2
+class Timed:
+    """One workload's steps timed on the device (see time_workload)."""
 
+
+def time_workload(args, name, dev, steps, warmup, block_size=None, partition_size=None):
+    """Generate the workload, upload it (``args.pool_copies`` copies of the
+    pool), and time ``steps`` decode steps back to back with one HIP event
+    pair around them, then ``min(steps, 50)`` single calls with an event pair
+    each (their spread).  Returns a Timed holding the workload, its device
+    tensors, the last step's output and the timings."""
     import numpy as np
     import torch
     import paged_kv_cache_269_amd as pa
     from paged_kv_cache_269_amd import workloads as W
 
-    if not torch.cuda.is_available():
-        print(json.dumps({"error": "no GPU visible"}))
-        return 1
-    dev = torch.device("cuda:0")
-    pa.load_library()
-
-    w = W.generate(args.config, poison=False, block_size=args.block_size)
-    part = w.partition_size if args.partition_size is None else args.partition_size
+    w = W.generate(name, poison=False, block_size=block_size)
+    part = w.partition_size if partition_size is None else partition_size
     d = W.to_device(w, dev)
     pools = [(d["k_cache"], d["v_cache"])]
     for _ in range(max(1, args.pool_copies) - 1):
@@ -496,6 +501,11 @@ def main(argv=None) -> int:
                                       w.scale, w.max_context_len, partition_size=part,
                                       workspace=ws, stream=stream)
 
+    def step(i):
+        if not (args.decode_only or fused):
+            reshape(i)
+        decode(i)
+
     if args.calibration_copy_mib > 0:
         n = args.calibration_copy_mib << 18           # float32 elements
         src = torch.ones(n, dtype=torch.float32, device=dev)
@@ -505,25 +515,24 @@ def main(argv=None) -> int:
         torch.cuda.synchronize()
         del src, dst
 
-    for i in range(args.warmup):
-        if not (args.decode_only or fused):
+    # every pool copy sees the KV write before timing starts (the last
+    # step's output then belongs to the written pool whichever copy it read)
+    for i in range(max(warmup, len(pools))):
+        if args.decode_only:
             reshape(i)
-        decode(i)
+        step(i)
     torch.cuda.synchronize()
 
     # Timed region: K steps back to back, one HIP event pair on the library's
     # stream around them (an event pair around every step would add its own
     # gaps between the launches: ~7 us per step measured).
-    K = args.steps
+    K = steps
     region = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     region[0].record(stream)
     for i in range(K):
-        j = args.warmup + i
-        if not (args.decode_only or fused):
-            reshape(j)
-        decode(j)
+        step(warmup + i)
     region[1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -534,17 +543,110 @@ def main(argv=None) -> int:
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(nspread)]
     for i in range(nspread):
-        j = args.warmup + K + i
+        j = warmup + K + i
         if not (args.decode_only or fused):
             reshape(j)
         ev[i][0].record(stream)
         decode(j)
         ev[i][1].record(stream)
     torch.cuda.synchronize()
-    dec_ms = np.array([a.elapsed_time(b) for a, b in ev])
-
+    t = Timed()
+    t.w, t.d, t.pools, t.ws, t.out, t.part = w, d, pools, ws, out, part
+    t.cascade, t.fused, t.stream = cascade, fused, stream
+    t.steps, t.wall, t.region_ms = K, wall, region_ms
+    t.dec_ms = np.array([a.elapsed_time(b) for a, b in ev])
     ab = W.algorithmic_bytes(w, unique=True)
-    step_bytes = ab["total"] + (0 if args.decode_only else W.reshape_bytes(w))
+    t.ab = ab
+    t.step_bytes = ab["total"] + (0 if args.decode_only else W.reshape_bytes(w))
+    return t
+
+
+def oracle_check(t):
+    """The last step's output against the float64 oracle over every output
+    row (the host pools with the oracle's own KV write): max-abs, rel-L2
+    over the whole tensor, and the oracle's time on all host threads."""
+    import numpy as np
+    import torch
+    import oracle
+
+    w = t.w
+    got = t.out.detach().cpu()
+    if w.dtype == "bf16":   # bf16 bits -> the float32 they stand for
+        got = (got.view(torch.uint16).numpy().astype(np.uint32) << 16).view(np.float32)
+    got = np.asarray(got.numpy() if isinstance(got, torch.Tensor) else got, np.float64)
+    oracle.reshape_and_cache(w.key, w.value, w.k_cache, w.v_cache, w.slot_mapping, w.dtype)
+    t0 = time.perf_counter()
+    ref = oracle.decode(w.q, w.k_cache, w.v_cache, w.block_tables, w.context_lens, w.scale,
+                        w.dtype)
+    dt = time.perf_counter() - t0
+    err = np.abs(got - ref)
+    nref = float(np.linalg.norm(ref))
+    return {"max_abs": float(err.max()), "rel_l2": float(np.linalg.norm(got - ref) / nref),
+            "rows": int(ref.shape[0] * ref.shape[1]),
+            "oracle_s": round(dt, 4), "oracle_GBps": round(t.ab["kv"] / dt / 1e9, 3),
+            "oracle_cores": oracle.max_threads(), "kind": "oracle"}
+
+
+def config_row(args, name, dev):
+    """One per-workload row: a few timed steps of the workload in its
+    benchmark configuration, the spread of single calls, the stored HBM
+    traffic, and the output against the oracle."""
+    import numpy as np
+    import torch
+
+    t = time_workload(args, name, dev, args.row_steps, 3)
+    ms = t.wall * 1e3 / t.steps
+    us_region = t.region_ms * 1e3 / t.steps
+    gbps = t.step_bytes / (us_region * 1e-6) / 1e9
+    row = {"entry": _entry(t, args), "partition_size": t.part, "num_seqs": t.w.num_seqs,
+           "steps": t.steps, "ms_per_step_wall": round(ms, 4),
+           "step_us_avg": round(us_region, 2),
+           "single_call_us_median": round(float(np.median(t.dec_ms)) * 1e3, 2),
+           "single_call_us_p10": round(float(np.percentile(t.dec_ms, 10)) * 1e3, 2),
+           "single_call_us_p90": round(float(np.percentile(t.dec_ms, 90)) * 1e3, 2),
+           "algorithmic_bytes_per_step": t.step_bytes, "GBps": round(gbps, 1),
+           "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
+           "seqs_per_s": round(t.w.num_seqs / (us_region * 1e-6), 1),
+           "hbm_traffic_bytes_per_step": stored_traffic(name)}
+    row["oracle"] = oracle_check(t)
+    del t
+    torch.cuda.empty_cache()
+    return row
+
+
+def _entry(t, args):
+    if t.fused and t.cascade:
+        return "pa_reshape_and_decode_cascade"
+    if t.fused:
+        return "pa_reshape_and_decode"
+    return "pa_paged_attention_decode_cascade" if t.cascade else "pa_paged_attention_decode"
+
+
+def main(argv=None) -> int:
+    args = parse_args(argv)
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU; "
+                                   f"--gpus {args.gpus} is not supported (no multi-GPU path "
+                                   "in this build)"}))
+        return 2
+
+    import numpy as np
+    import torch
+    import paged_kv_cache_269_amd as pa
+    from paged_kv_cache_269_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        return 1
+    dev = torch.device("cuda:0")
+    pa.load_library()
+
+    t = time_workload(args, args.config, dev, args.steps, args.warmup,
+                      block_size=args.block_size, partition_size=args.partition_size)
+    w, part, cascade, fused = t.w, t.part, t.cascade, t.fused
+    d, pools, ws, stream = t.d, t.pools, t.ws, t.stream
+    K, wall, region_ms, dec_ms = t.steps, t.wall, t.region_ms, t.dec_ms
+    ab, step_bytes = t.ab, t.step_bytes
     ms_per_step = wall * 1e3 / K
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     # Roofline of the step's launches over the timed region: one call of
@@ -575,10 +677,7 @@ def main(argv=None) -> int:
                    "context_len_mean": float(w.context_lens.mean()),
                    "context_len_max": int(w.max_context_len), "num_blocks": w.num_blocks,
                    "pool_copies": len(pools),
-                   "entry": ("pa_reshape_and_decode_cascade" if fused and cascade else
-                             "pa_reshape_and_decode" if fused else
-                             "pa_paged_attention_decode_cascade" if cascade
-                             else "pa_paged_attention_decode"),
+                   "entry": _entry(t, args),
                    "step": ("decode" if args.decode_only else
                             "KV write + decode in one call" if fused else
                             "reshape_and_cache + decode")
@@ -619,10 +718,25 @@ def main(argv=None) -> int:
         result["read_ceiling"] = read_ceiling(dev)
     if args.loop_steps > 0:
         del pools, d, ws
+        t.d = t.pools = t.ws = None
         torch.cuda.empty_cache()
         result["decode_loop"] = decode_loop(args, w, dev)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    rows_wanted = not (args.no_config_rows or args.decode_only or args.two_call
+                       or args.block_size or args.partition_size is not None
+                       or args.query_len or args.loop_steps or args.block_ops)
+    if rows_wanted:
+        # every workload: a few steps in its benchmark configuration, each
+        # checked against the oracle over its whole output
+        d = pools = ws = None
+        t.d = t.pools = t.ws = None
+        torch.cuda.empty_cache()
+        rows = {}
+        for name in W.CONFIG_ORDER:
+            print(f"[bench] row {name}", file=sys.stderr, flush=True)
+            rows[name] = config_row(args, name, dev)
+        result["configs"] = rows
     print(json.dumps(result), flush=True)
     return 0
 
