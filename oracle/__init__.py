@@ -27,7 +27,9 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
-_LIB = os.path.join(_HERE, "liboracle.so")
+# The in-tree build; ORACLE_LIB may name another build of oracle.c (the
+# sanitizer run of the CPU tests).
+_LIB = os.environ.get("ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 
 DTYPE_CODES = {"f32": 0, "f16": 1, "bf16": 2}
 

@@ -10,7 +10,6 @@
 #include <utility>
 #include <vector>
 
-#include "items.h"
 #include "launch.h"
 
 namespace {

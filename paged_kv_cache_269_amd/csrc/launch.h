@@ -128,4 +128,43 @@ hipError_t launch_multi_query(const MultiQueryArgs& a, int dtype, int head_dim,
 hipError_t launch_reduce(const ReduceArgs& a, int dtype, int head_dim, int num_seqs,
                          hipStream_t stream);
 
+// Host: compute units of the current device (cached per device; <= 0 on a
+// runtime error).
+inline int compute_units() {
+  static int per_device[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  const bool cacheable = dev >= 0 && dev < 64;
+  int cus = cacheable ? __atomic_load_n(&per_device[dev], __ATOMIC_RELAXED) : 0;
+  if (cus <= 0) {
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return -1;
+    if (cacheable && cus > 0) __atomic_store_n(&per_device[dev], cus, __ATOMIC_RELAXED);
+  }
+  return cus;
+}
+
+// Host: workgroups of `kernel` (block of `threads`) resident on the current
+// device at once, cached per device.  Returns <= 0 on a runtime error.
+struct ResidentCache {
+  int per_device[64] = {};
+};
+
+inline int resident_workgroups(const void* kernel, int threads, ResidentCache& c) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  const bool cacheable = dev >= 0 && dev < 64;
+  int resident = cacheable ? __atomic_load_n(&c.per_device[dev], __ATOMIC_RELAXED) : 0;
+  if (resident <= 0) {
+    int per_cu = 0;
+    const int cus = compute_units();
+    if (cus <= 0 ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess)
+      return -1;
+    resident = per_cu * cus;
+    if (cacheable && resident > 0) __atomic_store_n(&c.per_device[dev], resident, __ATOMIC_RELAXED);
+  }
+  return resident;
+}
+
 }  // namespace pa
