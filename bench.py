@@ -7,9 +7,10 @@ paged cache (decode kernel + split-K reduce).  Inputs are the seeded synthetic
 workload, resident in HBM before timing starts.
 
 Prints ONE JSON line.  ``value`` is whole-step throughput in GB/s of
-algorithmic bytes (K/V of every context token once -- shared prefix pages once
--- plus q in, out, the block-table entries used, the lengths, and the KV-write
-rows); ``seqs_per_s`` is sequences decoded per second.  ``roofline`` rates the
+algorithmic bytes (K/V of every context token once -- shared prefix pages once,
+each new token's row read once -- plus q in, out, the block-table entries used,
+the lengths, and the new rows written with their slots); ``seqs_per_s`` is
+sequences decoded per second.  ``roofline`` rates the
 decode kernel alone (its launches timed with HIP events on the library's
 stream) against the MI355X HBM peak; ``cpu_baseline`` is the float64 oracle
 on the host cores over a bounded sample of the same workload.
@@ -557,7 +558,7 @@ def time_workload(args, name, dev, steps, warmup, block_size=None, partition_siz
     t.dec_ms = np.array([a.elapsed_time(b) for a, b in ev])
     ab = W.algorithmic_bytes(w, unique=True)
     t.ab = ab
-    t.step_bytes = ab["total"] + (0 if args.decode_only else W.reshape_bytes(w))
+    t.step_bytes = ab["total"] if args.decode_only else W.step_bytes(w)
     return t
 
 

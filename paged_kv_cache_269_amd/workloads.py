@@ -350,9 +350,20 @@ def algorithmic_bytes(w: Workload, unique: bool = True) -> Dict[str, int]:
 
 
 def reshape_bytes(w: Workload) -> int:
-    """Bytes the KV write moves: read the new K/V rows, write them, read slots."""
+    """Bytes the KV write moves on its own: read the new K/V rows, write
+    them, read the slots."""
     rows = 2 * w.slot_mapping.shape[0] * w.num_kv_heads * w.head_dim * w.elem_bytes
     return 2 * rows + 8 * w.slot_mapping.shape[0]
+
+
+def step_bytes(w: Workload) -> int:
+    """Algorithmic bytes of one decode step (KV write + decode): those of
+    algorithmic_bytes -- whose K/V of every context token already include
+    each new token's row, read once -- plus the new rows written and the
+    slots read.  An implementation that writes the rows and then reads them
+    back from the cache moves more; the re-read is overhead."""
+    rows = 2 * w.slot_mapping.shape[0] * w.num_kv_heads * w.head_dim * w.elem_bytes
+    return algorithmic_bytes(w, unique=True)["total"] + rows + 8 * w.slot_mapping.shape[0]
 
 
 # ---------------------------------------------------------------------------
