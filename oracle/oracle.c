@@ -223,13 +223,15 @@ int oracle_decode_rows(double* out, double* out_m, double* out_l, const void* q,
   const int32_t D = head_dim;
   int status = ORC_OK;
 
+  /* the thread count applies to this call only (a clause, not the
+     process-wide default) */
 #ifdef _OPENMP
-  if (num_threads > 0) omp_set_num_threads(num_threads);
+  const int nthr = num_threads > 0 ? num_threads : omp_get_max_threads();
 #else
   (void)num_threads;
 #endif
 
-#pragma omp parallel
+#pragma omp parallel num_threads(nthr)
   {
     double* qv = (double*)malloc(sizeof(double) * D);
     double* z = NULL;

@@ -536,3 +536,15 @@ def test_multi_query_span_longer_than_context_gives_zero_rows():
     assert (out[:2] == 0).all()
     ref = oracle.multi_query(q, kc, vc, tables, cl, qs, 0.125, "f32")
     np.testing.assert_array_equal(out[2:], ref)
+
+
+def test_thread_count_applies_to_one_call():
+    """A call on one thread gives the same bits and leaves the default thread
+    count of later calls alone."""
+    w = W.generate("tiny")
+    before = oracle.max_threads()
+    a = oracle.decode(w.q, w.k_cache, w.v_cache, w.block_tables, w.context_lens, w.scale, w.dtype)
+    b = oracle.decode(w.q, w.k_cache, w.v_cache, w.block_tables, w.context_lens, w.scale, w.dtype,
+                      num_threads=1)
+    np.testing.assert_array_equal(a, b)
+    assert oracle.max_threads() == before
