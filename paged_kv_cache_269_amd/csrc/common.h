@@ -211,6 +211,17 @@ struct AddOp {
 struct MaxOp {
   __device__ __forceinline__ float operator()(float a, float b) const { return __builtin_fmaxf(a, b); }
 };
+// Maximum of operands that are never NaN (scores after masking, running
+// maxima).  The NaN-propagating form (v_maximum3_f32 on gfx950) needs no
+// quieting of its inputs, which fmaxf costs one extra instruction per
+// operand that the compiler cannot prove quiet (matrix-core results, lane
+// shuffles).
+__device__ __forceinline__ float max_nn(float a, float b) {
+  return __builtin_elementwise_maximum(a, b);
+}
+struct MaxNnOp {
+  __device__ __forceinline__ float operator()(float a, float b) const { return max_nn(a, b); }
+};
 
 // Reduction over aligned groups of N lanes (N in {2,4,8,16,32,64}); every
 // lane of a group receives the group's result.  Within a 16-lane row the

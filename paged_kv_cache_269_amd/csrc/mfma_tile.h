@@ -57,21 +57,34 @@ __device__ __forceinline__ f32x4 mfma_pv(const u32x2& a, const u32x2& b, const f
                                                  __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
 }
 
-// Two floats -> packed pair of 16-bit elements (round to nearest even).
+// Two floats -> packed pair of 16-bit elements (round to nearest even; one
+// v_cvt_pk_{f16,bf16}_f32).
 template <int DT>
 __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-  return (uint32_t)to_bits16<DT>(lo) | ((uint32_t)to_bits16<DT>(hi) << 16);
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  if constexpr (DT == kBF16)
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
+  else
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, f16x2));
 }
 
-// Sum of the four 16-bit weights of a packed P operand, exactly the values
-// the matrix core multiplies with.
+// acc + the two 16-bit elements of w (a dot product with (1, 1): the
+// products are exact).
 template <int DT>
-__device__ __forceinline__ float packed_sum(const u32x2& w) {
-  const uint32_t w0 = w[0], w1 = w[1];
-  float a, b, c, d;
-  unpack2<DT>(w0, a, b);
-  unpack2<DT>(w1, c, d);
-  return (a + b) + (c + d);
+__device__ __forceinline__ float add_pair(uint32_t w, float acc) {
+  if constexpr (DT == kBF16)
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w),
+                                           __builtin_bit_cast(bf16x2, 0x3f803f80u), acc, false);
+  else
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w), __builtin_bit_cast(f16x2, 0x3c003c00u),
+                                  acc, false);
+}
+
+// acc + the four 16-bit weights of a packed P operand, exactly the values the
+// matrix core multiplies with.
+template <int DT>
+__device__ __forceinline__ float packed_sum(const u32x2& w, float acc) {
+  return add_pair<DT>(w[1], add_pair<DT>(w[0], acc));
 }
 
 // 16-bit element k of a row slice held as EPL elements.
@@ -258,14 +271,14 @@ __device__ __forceinline__ void fold_tile(MfmaState<D>& st, const u32x4 (&qb)[D 
     sc[e] = sacc[e] * scale_log2;
     if constexpr (MASKED) sc[e] = ln.g + 4 * e < row_limit ? sc[e] : -INFINITY;
   }
-  float mb = __builtin_fmaxf(__builtin_fmaxf(sc[0], sc[1]), __builtin_fmaxf(sc[2], sc[3]));
-  mb = xor16_combine(mb, MaxOp{});
-  mb = xor32_combine(mb, MaxOp{});
+  float mb = max_nn(max_nn(sc[0], sc[1]), max_nn(sc[2], sc[3]));
+  mb = xor16_combine(mb, MaxNnOp{});
+  mb = xor32_combine(mb, MaxNnOp{});
   // The running max moves once a score passes it by more than kRescaleSlack,
   // so every weight stays below 2^kRescaleSlack.  The test is wave-uniform:
   // any row's rise rescales all.
   if (__builtin_amdgcn_ballot_w64(mb > st.m + kRescaleSlack) != 0) {
-    const float mn = __builtin_fmaxf(st.m, mb);
+    const float mn = max_nn(st.m, mb);
     const float alpha = mn == -INFINITY ? 1.f : fast_exp2(st.m - mn);
     st.lsum *= alpha;
     st.m = mn;
@@ -291,7 +304,7 @@ __device__ __forceinline__ void fold_tile(MfmaState<D>& st, const u32x4 (&qb)[D 
   const u32x2 pa{pack2<DT>(p[0], p[1]), pack2<DT>(p[2], p[3])};
   // The normaliser sums the weights as rounded for P.V, so numerator and
   // denominator weigh every token alike.
-  st.lsum += packed_sum<DT>(pa);
+  st.lsum = packed_sum<DT>(pa, st.lsum);
 #pragma unroll
   for (int jj = 0; jj < S::EPL; ++jj) st.o[jj] = mfma_pv<DT>(pa, vb[jj], st.o[jj]);
 }

@@ -368,13 +368,13 @@ __device__ __forceinline__ void fold_group(MfmaState<D> (&st)[RT],
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) x = __builtin_fmaxf(x, sc[r][t][e]);
-    mb[r] = xor16_combine(x, MaxOp{});
+      for (int e = 0; e < 4; ++e) x = max_nn(x, sc[r][t][e]);
+    mb[r] = xor16_combine(x, MaxNnOp{});
   }
 #pragma unroll
   for (int r = 0; r < RT; ++r) {
     // the largest raw score, scaled (scale_log2 >= 0 keeps it the largest)
-    const float mr = xor32_combine(mb[r], MaxOp{});
+    const float mr = xor32_combine(mb[r], MaxNnOp{});
     mb[r] = mr == -INFINITY ? -INFINITY : mr * scale_log2;
     grow = grow || mb[r] > st[r].m + kRescaleSlack;
   }
@@ -385,7 +385,7 @@ __device__ __forceinline__ void fold_group(MfmaState<D> (&st)[RT],
   if (__builtin_amdgcn_ballot_w64(grow) != 0) {
 #pragma unroll
     for (int r = 0; r < RT; ++r) {
-      const float mn = __builtin_fmaxf(st[r].m, mb[r]);
+      const float mn = max_nn(st[r].m, mb[r]);
       const float alpha = mn == -INFINITY ? 1.f : fast_exp2(st[r].m - mn);
       st[r].lsum *= alpha;
       st[r].m = mn;
@@ -416,7 +416,7 @@ __device__ __forceinline__ void fold_group(MfmaState<D> (&st)[RT],
         if constexpr (MASKED) p[e] = (none || sc[r][t][e] == -INFINITY) ? 0.f : p[e];
       }
       pa[r][t] = u32x2{pack2<DT>(p[0], p[1]), pack2<DT>(p[2], p[3])};
-      sum += packed_sum<DT>(pa[r][t]);  // the weights as rounded for P.V
+      sum = packed_sum<DT>(pa[r][t], sum);  // the weights as rounded for P.V
     }
     st[r].lsum += sum;
   }
