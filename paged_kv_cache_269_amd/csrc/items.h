@@ -32,8 +32,15 @@ struct TileIds {
   int id[H];
 };
 
-template <int BS>
-__device__ __forceinline__ TileIds<BS> tile_ids(const int32_t* bt, int j, int M) {
+// A block-table row read through the constant address space: the table does
+// not change during a launch, so the compiler may read it with scalar loads
+// even in kernels that also store to global memory (which it could
+// otherwise not prove free of aliasing with the table).
+typedef const __attribute__((address_space(4))) int32_t* TableRow;
+__device__ __forceinline__ TableRow table_row(const int32_t* p) { return (TableRow)p; }
+
+template <int BS, typename Ptr>
+__device__ __forceinline__ TileIds<BS> tile_ids(Ptr bt, int j, int M) {
   TileIds<BS> t;
   if constexpr (BS == 16) {
     t.id[0] = bt[j];

@@ -141,8 +141,9 @@ __global__ __launch_bounds__(NW * 64, 2) void multi_query_kernel(MultiQueryArgs 
   MfmaState<D> st[RT];
   static_for<0, RT>([&](auto rc) __attribute__((always_inline)) { st[decltype(rc)::value].reset(); });
 
+  const TableRow btc = table_row(bt);
   auto id_at = [&](int kk) __attribute__((always_inline)) {
-    return tile_ids<BS>(bt, j0 + min(kk, nk - 1) * NW, a.max_blocks_per_seq);
+    return tile_ids<BS>(btc, j0 + min(kk, nk - 1) * NW, a.max_blocks_per_seq);
   };
   // Descriptors of the wave's kk-th tile, its index and its token count
   // (tokens up to the item's last position, inside the pool).
@@ -262,8 +263,7 @@ __global__ __launch_bounds__(NW * 64, 2) void multi_query_kernel(MultiQueryArgs 
   });
 }
 
-// LDS of the wide kernel: per buffer and wave, one staged tile and its
-// token count.  K and V rows both keep their 16-byte chunks permuted within
+// LDS of the wide kernel: per buffer and wave, one staged tile.  K and V rows both keep their 16-byte chunks permuted within
 // the row (kswz), so the column-wise operand reads of 16 rows spread over
 // the banks.
 template <int D, typename VT, int NW>
@@ -273,7 +273,6 @@ struct WideLds {
     u32x4 v[kBlockSize * D / 8];  // the same layout for V
   };
   Tile t[2][NW];
-  int lim[2][NW];
 };
 
 // Position of K chunk c of token row r in a wide tile: chunks are permuted
@@ -538,18 +537,32 @@ __global__ __launch_bounds__(NW * 64, 2) void multi_query_wide_kernel(MultiQuery
   const int je = min(jb + a.part_blocks, nblocks);
   const int ngroups = je > jb ? (je - jb + NW - 1) / NW : 0;
   // Tile of group g this wave loads (index clamped into the item).
-  auto id_at = [&](int g) __attribute__((always_inline)) {
-    return tile_ids<BS>(bt, min(jb + g * NW + w, je - 1), a.max_blocks_per_seq);
+  // Every wave reads the block ids of all NW tiles of a group (scalar loads,
+  // two groups ahead): it loads its own tile and knows every tile's token
+  // count without a round trip through LDS.
+  const TableRow btc = table_row(bt);
+  struct GroupIds {
+    TileIds<BS> t[NW];
   };
-  // This wave's tile of group g into LDS buffer `b`, with its token count.
+  auto ids_at = [&](int g) __attribute__((always_inline)) {
+    GroupIds r;
+#pragma unroll
+    for (int t = 0; t < NW; ++t)
+      r.t[t] = tile_ids<BS>(btc, min(jb + g * NW + t, je - 1), a.max_blocks_per_seq);
+    return r;
+  };
+  // the wave's own tile of group g (a load of its own: picking it out of a
+  // GroupIds by the wave index would index an array at run time)
+  auto id_at = [&](int g) __attribute__((always_inline)) {
+    return tile_ids<BS>(btc, min(jb + g * NW + w, je - 1), a.max_blocks_per_seq);
+  };
+  // This wave's tile of group g into LDS buffer `b`.
   u32x4* const lds_k[2] = {sm.t[0][w].k, sm.t[1][w].k};
   u32x4* const lds_v[2] = {reinterpret_cast<u32x4*>(sm.t[0][w].v),
                            reinterpret_cast<u32x4*>(sm.t[1][w].v)};
-  int* const lds_lim[2] = {&sm.lim[0][w], &sm.lim[1][w]};
   auto load = [&](int g, const TileIds<BS>& ids, int b) __attribute__((always_inline)) {
     const int jt = jb + g * NW + w;
     const bool ok = g < ngroups && jt < je;
-    const int limit = ok ? tile_limit<BS>(a, ids, span - jt * kBlockSize) : 0;
     const TileDesc<BS, S::TILE_BYTES> desc = tile_desc<BS, S::TILE_BYTES>(a, ids, jt, kvh, ok);
     // Buffer loads with the LDS destination: lane l of a load writes the 16
     // bytes at slot 64 jj + l of the load's KiB, no registers involved.  A K
@@ -570,13 +583,13 @@ __global__ __launch_bounds__(NW * 64, 2) void multi_query_wide_kernel(MultiQuery
         load16_to_lds<PA_KV_LOAD_POLICY>(desc.v[h], lds_v[b] + jj * 64, voff);
       }
     });
-    if (lane == 0) *lds_lim[b] = limit;
   };
 
   if (ngroups > 0) {
     // Group g + 1 streams into the other buffer while group g is folded;
     // a wait for the wave's own loads and one barrier per group.
     load(0, id_at(0), 0);
+    GroupIds ids_g = ids_at(0);
     TileIds<BS> next_id = id_at(1);
     wait_lds_loads();
     __syncthreads();
@@ -585,10 +598,14 @@ __global__ __launch_bounds__(NW * 64, 2) void multi_query_wide_kernel(MultiQuery
       const TileIds<BS> id = next_id;
       next_id = id_at(g + 2);
       load(g + 1, id, b ^ 1);  // buffer b ^ 1 was last read before the previous barrier
+      const int g_first = (jb + g * NW) * kBlockSize;  // first token of the group
       int lims[NW];
 #pragma unroll
-      for (int t = 0; t < NW; ++t) lims[t] = __builtin_amdgcn_readfirstlane(sm.lim[b][t]);
-      const int g_first = (jb + g * NW) * kBlockSize;  // first token of the group
+      for (int t = 0; t < NW; ++t) {
+        const int jt = jb + g * NW + t;
+        lims[t] = jt < je ? tile_limit<BS>(a, ids_g.t[t], span - jt * kBlockSize) : 0;
+      }
+      ids_g = ids_at(g + 1);
       bool any = false, whole = true;
 #pragma unroll
       for (int t = 0; t < NW; ++t) whole = whole && lims[t] == kBlockSize;

@@ -132,7 +132,8 @@ __global__ __launch_bounds__(NW * 64) void prefix_kernel(DecodeArgs a, PrefixOut
   u32x4 kr[DEPTH][S::NJ];
   VT vr[DEPTH][4];
   int lim[DEPTH];
-  auto id_at = [&](int kk) -> int { return bt[w + min(kk, max(nk - 1, 0)) * NW]; };
+  const TableRow btc = table_row(bt);
+  auto id_at = [&](int kk) -> int { return btc[w + min(kk, max(nk - 1, 0)) * NW]; };
   auto issue = [&](int kk, int bid, int slot) {
     const bool ok = kk < nk && (uint32_t)bid < (uint32_t)a.num_blocks_i32;
     lim[slot] = ok ? kBlockSize : 0;
