@@ -263,16 +263,17 @@ __global__ __launch_bounds__(NW * 64, 2) void multi_query_kernel(MultiQueryArgs 
   });
 }
 
-// LDS of the wide kernel: per buffer and wave, one staged tile.  K and V rows both keep their 16-byte chunks permuted within
-// the row (kswz), so the column-wise operand reads of 16 rows spread over
-// the banks.
-template <int D, typename VT, int NW>
-struct WideLds {
-  struct Tile {
-    u32x4 k[kBlockSize * D / 8];  // 16-byte chunk c of row r at r * D/8 + (c ^ r % (D/8))
-    u32x4 v[kBlockSize * D / 8];  // the same layout for V
-  };
-  Tile t[2][NW];
+// One staged tile of the wide kernel in LDS.  K and V rows keep their
+// 16-byte chunks permuted within the row (kswz), so the column-wise operand
+// reads of 16 rows spread over the banks.  The kernel keeps its two buffers
+// of NW tiles in two separate LDS variables and names the one it touches at
+// compile time: the compiler can then tell the loads into one buffer from
+// the reads of the other, instead of waiting for every load in flight before
+// a read.
+template <int D>
+struct WideTile {
+  u32x4 k[kBlockSize * D / 8];  // 16-byte chunk c of row r at r * D/8 + (c ^ r % (D/8))
+  u32x4 v[kBlockSize * D / 8];  // the same layout for V
 };
 
 // Position of K chunk c of token row r in a wide tile: chunks are permuted
@@ -476,7 +477,7 @@ __global__ __launch_bounds__(NW * 64, 2) void multi_query_wide_kernel(MultiQuery
   using VT = typename S::VT;
   constexpr int EPL = S::EPL;
   constexpr int ROWS = NW * RT * 16;
-  __shared__ WideLds<D, VT, NW> sm;
+  __shared__ WideTile<D> buf0[NW], buf1[NW];
   const DecodeArgs& a = ma.d;
   const int G = a.num_q_heads / a.num_kv_heads;
   const int kvh = blockIdx.x % a.num_kv_heads, unit = blockIdx.x / a.num_kv_heads;
@@ -556,11 +557,16 @@ __global__ __launch_bounds__(NW * 64, 2) void multi_query_wide_kernel(MultiQuery
   auto id_at = [&](int g) __attribute__((always_inline)) {
     return tile_ids<BS>(btc, min(jb + g * NW + w, je - 1), a.max_blocks_per_seq);
   };
-  // This wave's tile of group g into LDS buffer `b`.
-  u32x4* const lds_k[2] = {sm.t[0][w].k, sm.t[1][w].k};
-  u32x4* const lds_v[2] = {reinterpret_cast<u32x4*>(sm.t[0][w].v),
-                           reinterpret_cast<u32x4*>(sm.t[1][w].v)};
-  auto load = [&](int g, const TileIds<BS>& ids, int b) __attribute__((always_inline)) {
+  // LDS buffer B (0 or 1, known at compile time).
+  auto buffer = [&](auto bc) __attribute__((always_inline)) {
+    if constexpr (decltype(bc)::value == 0)
+      return buf0;
+    else
+      return buf1;
+  };
+  // This wave's tile of group g into LDS buffer bc.
+  auto load = [&](int g, const TileIds<BS>& ids, auto bc) __attribute__((always_inline)) {
+    WideTile<D>* const dst = buffer(bc) + w;
     const int jt = jb + g * NW + w;
     const bool ok = g < ngroups && jt < je;
     const TileDesc<BS, S::TILE_BYTES> desc = tile_desc<BS, S::TILE_BYTES>(a, ids, jt, kvh, ok);
@@ -576,28 +582,26 @@ __global__ __launch_bounds__(NW * 64, 2) void multi_query_wide_kernel(MultiQuery
       const int r = p / S::CPR, c = (p % S::CPR) ^ (r % S::CPR);
       const int koff = (r * S::CPR + c) * 16 - h * Desc::HB, voff = koff;  // both kswz
       if (ma.reread) {
-        load16_to_lds<PA_SHARED_LOAD_POLICY>(desc.k[h], lds_k[b] + jj * 64, koff);
-        load16_to_lds<PA_SHARED_LOAD_POLICY>(desc.v[h], lds_v[b] + jj * 64, voff);
+        load16_to_lds<PA_SHARED_LOAD_POLICY>(desc.k[h], dst->k + jj * 64, koff);
+        load16_to_lds<PA_SHARED_LOAD_POLICY>(desc.v[h], dst->v + jj * 64, voff);
       } else {
-        load16_to_lds<PA_KV_LOAD_POLICY>(desc.k[h], lds_k[b] + jj * 64, koff);
-        load16_to_lds<PA_KV_LOAD_POLICY>(desc.v[h], lds_v[b] + jj * 64, voff);
+        load16_to_lds<PA_KV_LOAD_POLICY>(desc.k[h], dst->k + jj * 64, koff);
+        load16_to_lds<PA_KV_LOAD_POLICY>(desc.v[h], dst->v + jj * 64, voff);
       }
     });
   };
 
-  if (ngroups > 0) {
-    // Group g + 1 streams into the other buffer while group g is folded;
-    // a wait for the wave's own loads and one barrier per group.
-    load(0, id_at(0), 0);
-    GroupIds ids_g = ids_at(0);
-    TileIds<BS> next_id = id_at(1);
-    wait_lds_loads();
-    __syncthreads();
-    for (int g = 0; g < ngroups; ++g) {
-      const int b = g & 1;
+  GroupIds ids_g;
+  TileIds<BS> next_id;
+  // Group g, held in buffer bc: load group g + 1 into the other buffer, fold
+  // group g, wait for the wave's own loads and meet the other waves.
+  auto step = [&](int g, auto bc) __attribute__((always_inline)) {
+      constexpr int B = decltype(bc)::value;
+      WideTile<D>* const tiles = buffer(bc);
       const TileIds<BS> id = next_id;
       next_id = id_at(g + 2);
-      load(g + 1, id, b ^ 1);  // buffer b ^ 1 was last read before the previous barrier
+      // the other buffer was last read before the previous barrier
+      load(g + 1, id, std::integral_constant<int, 1 - B>{});
       const int g_first = (jb + g * NW) * kBlockSize;  // first token of the group
       int lims[NW];
 #pragma unroll
@@ -622,15 +626,25 @@ __global__ __launch_bounds__(NW * 64, 2) void multi_query_wide_kernel(MultiQuery
           constexpr int t0 = decltype(hc)::value * FT;
           const int(&lh)[FT] = *reinterpret_cast<const int(*)[FT]>(&lims[t0]);
           if (whole)
-            fold_group<DT, D, FT, RT, false>(st, qb, pos_n, &sm.t[b][t0], lh,
-                                                     g_first + t0 * kBlockSize, sl, ln);
+            fold_group<DT, D, FT, RT, false>(st, qb, pos_n, tiles + t0, lh,
+                                             g_first + t0 * kBlockSize, sl, ln);
           else
-            fold_group<DT, D, FT, RT, true>(st, qb, pos_n, &sm.t[b][t0], lh,
-                                                    g_first + t0 * kBlockSize, sl, ln);
+            fold_group<DT, D, FT, RT, true>(st, qb, pos_n, tiles + t0, lh,
+                                            g_first + t0 * kBlockSize, sl, ln);
         });
       }
       wait_lds_loads();
-      __syncthreads();  // group g + 1 in buffer b ^ 1; every wave done with buffer b
+      __syncthreads();  // group g + 1 in the other buffer; every wave done with this one
+  };
+  if (ngroups > 0) {
+    load(0, id_at(0), std::integral_constant<int, 0>{});
+    ids_g = ids_at(0);
+    next_id = id_at(1);
+    wait_lds_loads();
+    __syncthreads();
+    for (int g = 0; g < ngroups; g += 2) {
+      step(g, std::integral_constant<int, 0>{});
+      if (g + 1 < ngroups) step(g + 1, std::integral_constant<int, 1>{});
     }
   }
 
