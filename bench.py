@@ -712,7 +712,12 @@ def main(argv=None) -> int:
                      "algorithmic_bytes_per_step": launch_bytes},
     }
     if args.query_len > 0:
-        result["multi_query"] = multi_query_bench(args, w, d, pools, part, stream)
+        # the library's suggested partition for multi-token queries, unless
+        # one is given (the decode's partitions are sized for one row per head)
+        import paged_kv_cache_269_amd as pa
+        mq_part = part if args.partition_size is not None else pa.multi_query_partition_size(
+            w.num_seqs, w.num_q_heads, w.num_kv_heads, args.query_len, w.max_context_len)
+        result["multi_query"] = multi_query_bench(args, w, d, pools, mq_part, stream)
     if args.block_ops:
         result["block_ops"] = block_ops(w, dev)
     if args.read_ceiling:

@@ -329,6 +329,21 @@ size_t pa_multi_query_workspace_bytes(int32_t num_query_tokens, int32_t num_q_he
                                       int32_t partition_size);
 
 /*
+ * A partition size for pa_paged_attention_multi_query (host only, no
+ * device work): 0 (one pass) when the one-pass items -- (sequence, KV head,
+ * unit of up to 128 query rows) -- already number at least four per compute
+ * unit of the current device; else the longest power-of-two partition that
+ * still makes that many items at max_context_len, and no shorter than 16
+ * tokens per query row of an item (512 at least), so that the float partials
+ * stay under 1/16 of the K/V bytes each item reads; 0 when that covers
+ * max_context_len.  The result is a suggestion: any valid partition_size
+ * gives the same attention up to rounding.  Returns 0 for invalid arguments.
+ */
+int32_t pa_multi_query_partition_size(int32_t num_seqs, int32_t num_q_heads,
+                                      int32_t num_kv_heads, int32_t max_query_len,
+                                      int32_t max_context_len);
+
+/*
  * Host-side check of query offsets (host pointers): query_start[0] = 0,
  * query_start[num_seqs] = num_query_tokens, every span length n_s in
  * [0, max_query_len] and, when context_lens is not NULL, n_s <=

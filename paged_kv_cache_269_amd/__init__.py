@@ -17,6 +17,7 @@ from ._binding import (  # noqa: F401
     decode_workspace_bytes,
     lib_path,
     load_library,
+    multi_query_partition_size,
     multi_query_workspace,
     multi_query_workspace_bytes,
     paged_attention_decode,
@@ -43,7 +44,7 @@ from ._binding import (  # noqa: F401
 __all__ = [
     "BlockManager", "KVCacheExhausted", "PagedAttnError", "cascade_workspace",
     "cascade_workspace_bytes", "copy_blocks", "decode_workspace", "decode_workspace_bytes",
-    "lib_path", "load_library", "multi_query_workspace", "multi_query_workspace_bytes",
+    "lib_path", "load_library", "multi_query_partition_size", "multi_query_workspace", "multi_query_workspace_bytes",
     "paged_attention_decode", "paged_attention_decode_cascade", "paged_attention_multi_query",
     "paged_attention_reduce", "reshape_and_cache", "reshape_and_decode", "reshape_and_decode_cascade",
     "reshape_and_decode_static", "STATIC_SCRATCH_BYTES", "status_string",

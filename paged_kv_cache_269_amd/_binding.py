@@ -56,6 +56,7 @@ EXPORTS = {
                                                       _I32, _I32, _I32, _I32, _I32, _I64, _F32,
                                                       _I32, _I32, _I32, _I32, _P, _SZ, _P]),
     "pa_multi_query_workspace_bytes": (ctypes.c_size_t, [_I32, _I32, _I32, _I32, _I32]),
+    "pa_multi_query_partition_size": (_I32, [_I32, _I32, _I32, _I32, _I32]),
     "pa_validate_query_start_host": (ctypes.c_int, [_P, _P, _I32, _I32, _I32]),
     "pa_validate_tables_host": (ctypes.c_int, [_P, _P, _I32, _I32, _I64, _I32]),
     "pa_validate_slots_host": (ctypes.c_int, [_P, _I32, _I64, _I32]),
@@ -361,6 +362,13 @@ def multi_query_workspace_bytes(num_query_tokens: int, num_q_heads: int, head_di
                                 max_context_len: int, partition_size: int) -> int:
     return int(load_library().pa_multi_query_workspace_bytes(
         num_query_tokens, num_q_heads, head_dim, max_context_len, partition_size))
+
+
+def multi_query_partition_size(num_seqs: int, num_q_heads: int, num_kv_heads: int,
+                               max_query_len: int, max_context_len: int) -> int:
+    """Suggested partition_size for paged_attention_multi_query (0: one pass)."""
+    return int(load_library().pa_multi_query_partition_size(
+        num_seqs, num_q_heads, num_kv_heads, max_query_len, max_context_len))
 
 
 def multi_query_workspace(num_query_tokens: int, num_q_heads: int, head_dim: int,

@@ -333,6 +333,28 @@ size_t pa_multi_query_workspace_bytes(int32_t num_query_tokens, int32_t num_q_he
   return w.total ? w.total + align256((size_t)num_query_tokens * sizeof(int32_t)) : 0;
 }
 
+int32_t pa_multi_query_partition_size(int32_t num_seqs, int32_t num_q_heads,
+                                      int32_t num_kv_heads, int32_t max_query_len,
+                                      int32_t max_context_len) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads ||
+      max_query_len <= 0 || max_context_len <= 0)
+    return 0;
+  // items of one pass: (sequence, KV head, unit of up to 128 rows)
+  const int64_t rows = (int64_t)max_query_len * (num_q_heads / num_kv_heads);
+  const int64_t item_rows = std::min<int64_t>(rows, 128);
+  const int64_t one_pass = (int64_t)num_seqs * num_kv_heads * ceil_div(rows, 128);
+  const int cus = pa::compute_units();
+  const int64_t target = 4LL * (cus > 0 ? cus : 256);
+  if (one_pass >= target) return 0;
+  // a partition of at least 16 tokens per row of its item keeps the float
+  // partials under 1/16 of the K/V bytes it reads; the longest such partition
+  // that still yields `target` items (counted at max_context_len)
+  int64_t part = 512;
+  while (part < 16 * item_rows) part *= 2;
+  while (one_pass * ceil_div(max_context_len, 2 * part) >= target) part *= 2;
+  return part >= max_context_len ? 0 : (int32_t)part;
+}
+
 int pa_paged_attention_multi_query(void* out, const void* q, const void* k_cache,
                                    const void* v_cache, const int32_t* block_tables,
                                    const int32_t* context_lens, const int32_t* query_start,

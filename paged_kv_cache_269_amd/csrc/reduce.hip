@@ -8,7 +8,8 @@
 // partitions processed in parallel; it runs after the decode kernel on the
 // same stream.
 //
-// One workgroup (512 lanes) per (query head, sequence): of up to 512
+// Up to 64 partitions per row: one wave per row (reduce_rows_kernel).
+// More: one workgroup (512 lanes) per (query head, sequence): of up to 512
 // partitions at a time, those with weight are compacted into LDS (index and
 // weight; slots left empty by a kernel that folded several partitions into
 // one are never read), then 512 / head_dim lane groups each sweep a share of
@@ -124,10 +125,74 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(ReduceArgs a) {
   }
 }
 
+// Many rows with few partitions each (multi-token queries: a row per query
+// token and head): one wave per row, kRowsPerGroup rows per workgroup.  Lane
+// l holds columns kCols l .. kCols l + kCols - 1; partition p's weight is
+// computed by lane p % 64 and broadcast; kRowUnroll partition rows are
+// loaded at a time.  Slots without weight (empty, possibly never written)
+// are dropped by selection, never multiplied in.
+constexpr int kRowsPerGroup = 4;
+constexpr int kRowUnroll = 4;
+constexpr int kRowsMaxPartitions = 64;
+
+template <int DT, int D>
+__global__ __launch_bounds__(64 * kRowsPerGroup) void reduce_rows_kernel(ReduceArgs a,
+                                                                          int num_rows) {
+  constexpr int C = D / 64;
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * kRowsPerGroup + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (row >= num_rows) return;
+  const int s = row / a.num_q_heads;
+  int L = a.context_lens[s];
+  L = L < 0 ? 0 : (L > a.max_len ? a.max_len : L);
+  const int P = (L + a.partition_size - 1) / a.partition_size;
+  if (a.skip_single && P <= 1) return;
+  const int64_t base = (int64_t)row * a.max_partitions;
+
+  // P <= kRowsMaxPartitions: one partition per lane
+  const bool mine = lane < P;
+  const float l = mine ? a.exp_sums[base + lane] : 0.f;
+  const float m = mine ? a.max_logits[base + lane] : -INFINITY;
+  const float M = group_reduce<64>(l > 0.f ? m : -INFINITY, MaxOp{});
+  const float wv = l > 0.f ? l * fast_exp2((m - M) * kLog2e) : 0.f;
+  const float wsum = group_sum<64>(wv);
+
+  float o[C];
+#pragma unroll
+  for (int c = 0; c < C; ++c) o[c] = 0.f;
+  const float* __restrict__ t0 = a.tmp_out + base * D + C * lane;
+  for (int p0 = 0; p0 < P; p0 += kRowUnroll) {
+    float t[kRowUnroll][C], w[kRowUnroll];
+#pragma unroll
+    for (int u = 0; u < kRowUnroll; ++u) {  // loads issued unconditionally (index kept in range)
+      const int p = min(p0 + u, P - 1);
+      w[u] = p0 + u < P ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                                        __builtin_bit_cast(int, wv), p))
+                        : 0.f;
+#pragma unroll
+      for (int c = 0; c < C; ++c) t[u][c] = t0[(int64_t)p * D + c];
+    }
+#pragma unroll
+    for (int u = 0; u < kRowUnroll; ++u)
+#pragma unroll
+      for (int c = 0; c < C; ++c) o[c] += w[u] > 0.f ? w[u] * t[u][c] : 0.f;
+  }
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+#pragma unroll
+  for (int c = 0; c < C; ++c) store_elem<DT>(a.out, (int64_t)row * D + C * lane + c, o[c] * inv);
+}
+
 template <int DT, int D>
 hipError_t launch_typed(const ReduceArgs& a, int num_seqs, hipStream_t stream) {
-  hipLaunchKernelGGL((reduce_kernel<DT, D>), dim3(a.num_q_heads, num_seqs), dim3(kThreads), 0,
-                     stream, a);
+  if (a.max_partitions <= kRowsMaxPartitions) {
+    const int rows = num_seqs * a.num_q_heads;
+    hipLaunchKernelGGL((reduce_rows_kernel<DT, D>),
+                       dim3((rows + kRowsPerGroup - 1) / kRowsPerGroup), dim3(64 * kRowsPerGroup),
+                       0, stream, a, rows);
+  } else {
+    hipLaunchKernelGGL((reduce_kernel<DT, D>), dim3(a.num_q_heads, num_seqs), dim3(kThreads), 0,
+                       stream, a);
+  }
   return hipGetLastError();
 }
 

@@ -125,6 +125,38 @@ def _cascade(lib, **kw):
                                                  a["maxlen"], a["ws"], a["wsb"], a["stream"])
 
 
+def test_multi_query_partition_size(hiplib):
+    """The suggested multi-query partition follows its stated rule (no device
+    here: the library assumes 256 compute units, target 1024 items)."""
+    f = hiplib.multi_query_partition_size
+    target = 4 * 256
+
+    def items(B, Hq, Hkv, n, L, part):
+        rows = n * (Hq // Hkv)
+        one = B * Hkv * -(-rows // 128)
+        return one * (-(-L // part) if part else 1), one, rows
+
+    cases = [(8, 64, 8, 16, 131072), (8, 64, 8, 4, 131072), (2, 32, 32, 8, 40000),
+             (1, 64, 8, 64, 1 << 20), (4, 8, 8, 2, 20000), (16, 64, 8, 16, 65536)]
+    for B, Hq, Hkv, n, L in cases:
+        part = f(B, Hq, Hkv, n, L)
+        tot, one, rows = items(B, Hq, Hkv, n, L, part)
+        assert part > 0 and part < L, (B, Hq, Hkv, n, L, part)
+        assert part & (part - 1) == 0 and part % 16 == 0
+        assert part >= max(512, 16 * min(rows, 128))
+        # the longest such partition that still makes `target` items, or the
+        # shortest allowed one when none does
+        assert tot >= target or part == max(512, 1 << (16 * min(rows, 128) - 1).bit_length())
+        assert items(B, Hq, Hkv, n, L, 2 * part)[0] < target
+    # enough items in one pass, or one partition covering the context: one pass
+    assert f(128, 64, 8, 16, 8192) == 0
+    assert f(64, 32, 32, 8, 2048) == 0
+    assert f(2, 64, 8, 16, 1000) == 0
+    # invalid arguments
+    assert f(0, 64, 8, 16, 4096) == 0 and f(8, 64, 7, 16, 4096) == 0
+    assert f(8, 64, 8, 0, 4096) == 0 and f(8, 64, 8, 16, 0) == 0
+
+
 def test_cascade_argument_checks_and_workspace(hiplib):
     lib = hiplib.load_library()
     f = lib.pa_cascade_workspace_bytes
