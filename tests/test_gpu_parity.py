@@ -148,13 +148,16 @@ def test_shared_prefix_equals_private_copies_on_gpu(cuda):
     assert np.array_equal(tensor_to_np(out, w.dtype), out_shared)
 
 
-def test_reduce_matches_oracle_merge(cuda):
+@pytest.mark.parametrize("max_parts", [64, 300])
+def test_reduce_matches_oracle_merge(cuda, max_parts):
+    """Both reduce kernels: up to 64 partitions a row (one wave per row) and
+    more (one workgroup per row)."""
     import paged_kv_cache_269_amd as pa
     for dtype, D, part in (("bf16", 128, 512), ("f32", 64, 64), ("f16", 128, 16)):
-        announce("reduce", dtype, D, part)
+        announce("reduce", dtype, D, part, "max partitions", max_parts)
         p = W.generate_partials(seed=9, num_seqs=7, num_q_heads=5, head_dim=D,
                                 partition_size=part, lens=[0, 1, part, part + 1, 3 * part,
-                                                           40 * part + 7, 300 * part])
+                                                           40 * part + 7, max_parts * part])
         B, Hq, P = p.max_logits.shape
         R = B * Hq
         ref = oracle.lse_merge(np.nan_to_num(p.max_logits.reshape(R, P)),
