@@ -80,6 +80,17 @@ __device__ __forceinline__ float add_pair(uint32_t w, float acc) {
                                   acc, false);
 }
 
+// The residuals p[e] - (p[e] as packed in pa), packed the same way: the
+// subtraction is exact in fp32, so pa + residual holds each weight to about
+// twice the 16-bit precision.
+template <int DT>
+__device__ __forceinline__ u32x2 residual_pack(const float (&p)[4], const u32x2& pa) {
+  float r[4];
+  unpack2<DT>(pa[0], r[0], r[1]);
+  unpack2<DT>(pa[1], r[2], r[3]);
+  return u32x2{pack2<DT>(p[0] - r[0], p[1] - r[1]), pack2<DT>(p[2] - r[2], p[3] - r[3])};
+}
+
 // acc + the four 16-bit weights of a packed P operand, exactly the values the
 // matrix core multiplies with.
 template <int DT>
@@ -307,6 +318,16 @@ __device__ __forceinline__ void fold_tile(MfmaState<D>& st, const u32x4 (&qb)[D 
   st.lsum = packed_sum<DT>(pa, st.lsum);
 #pragma unroll
   for (int jj = 0; jj < S::EPL; ++jj) st.o[jj] = mfma_pv<DT>(pa, vb[jj], st.o[jj]);
+  if constexpr (DT == kBF16) {
+    // bf16 weights carry 8 significant bits: one weight's rounding moves the
+    // output by up to 2^-9 of the spread of V, past the 1e-2 bound in the
+    // tail of N(0,1) data.  The residual of each weight goes through a second
+    // product, so P.V and the normaliser see the weights to ~2^-17.
+    const u32x2 pl = residual_pack<DT>(p, pa);
+    st.lsum = packed_sum<DT>(pl, st.lsum);
+#pragma unroll
+    for (int jj = 0; jj < S::EPL; ++jj) st.o[jj] = mfma_pv<DT>(pl, vb[jj], st.o[jj]);
+  }
 }
 
 // Fold one tile (`limit` of its 16 tokens in the context) into the state:

@@ -400,7 +400,11 @@ __device__ __forceinline__ void fold_group(MfmaState<D> (&st)[RT],
         for (int e = 0; e < 4; ++e) st[r].o[jj][e] *= arow[e];
     }
   }
-  u32x2 pa[RT][NT];
+  // bf16 weights also carry their residuals (a second P.V product): one
+  // weight's 8-bit rounding moves the output by up to 2^-9 of the spread of
+  // V, past the 1e-2 bound in the tail of N(0,1) data (see fold_tile).
+  constexpr bool SPLIT = DT == kBF16;
+  u32x2 pa[RT][NT], pl[RT][NT];
 #pragma unroll
   for (int r = 0; r < RT; ++r) {
     const bool none = MASKED && st[r].m == -INFINITY;  // no valid token of this row so far
@@ -417,6 +421,10 @@ __device__ __forceinline__ void fold_group(MfmaState<D> (&st)[RT],
       }
       pa[r][t] = u32x2{pack2<DT>(p[0], p[1]), pack2<DT>(p[2], p[3])};
       sum = packed_sum<DT>(pa[r][t], sum);  // the weights as rounded for P.V
+      if constexpr (SPLIT) {
+        pl[r][t] = residual_pack<DT>(p, pa[r][t]);
+        sum = packed_sum<DT>(pl[r][t], sum);
+      }
     }
     st[r].lsum += sum;
   }
@@ -437,10 +445,13 @@ __device__ __forceinline__ void fold_group(MfmaState<D> (&st)[RT],
   };
 #pragma unroll
   for (int t = 0; t < NT; t += 2) {
-    u32x4 pp[RT];
+    u32x4 pp[RT], ppl[RT];
 #pragma unroll
-    for (int r = 0; r < RT; ++r)
+    for (int r = 0; r < RT; ++r) {
       pp[r] = u32x4{pa[r][t][0], pa[r][t][1], pa[r][t + 1][0], pa[r][t + 1][1]};
+      if constexpr (SPLIT)
+        ppl[r] = u32x4{pl[r][t][0], pl[r][t][1], pl[r][t + 1][0], pl[r][t + 1][1]};
+    }
 #pragma unroll
     for (int jj = 0; jj < D / 16; ++jj) {
       u32x2 v0 = lds_read_tr16(reinterpret_cast<const char*>(tiles[t].v) + tr_off(jj));
@@ -457,7 +468,10 @@ __device__ __forceinline__ void fold_group(MfmaState<D> (&st)[RT],
       }
       const u32x4 vb{v0[0], v0[1], v1[0], v1[1]};
 #pragma unroll
-      for (int r = 0; r < RT; ++r) st[r].o[jj] = mfma_qk<DT>(pp[r], vb, st[r].o[jj]);
+      for (int r = 0; r < RT; ++r) {
+        st[r].o[jj] = mfma_qk<DT>(pp[r], vb, st[r].o[jj]);
+        if constexpr (SPLIT) st[r].o[jj] = mfma_qk<DT>(ppl[r], vb, st[r].o[jj]);
+      }
     }
   }
 }
