@@ -316,17 +316,22 @@ __device__ __forceinline__ void fold_tile(MfmaState<D>& st, const u32x4 (&qb)[D 
   // The normaliser sums the weights as rounded for P.V, so numerator and
   // denominator weigh every token alike.
   st.lsum = packed_sum<DT>(pa, st.lsum);
-#pragma unroll
-  for (int jj = 0; jj < S::EPL; ++jj) st.o[jj] = mfma_pv<DT>(pa, vb[jj], st.o[jj]);
   if constexpr (DT == kBF16) {
     // bf16 weights carry 8 significant bits: one weight's rounding moves the
-    // output by up to 2^-9 of the spread of V, past the 1e-2 bound in the
-    // tail of N(0,1) data.  The residual of each weight goes through a second
-    // product, so P.V and the normaliser see the weights to ~2^-17.
+    // output by up to 2^-8 of the spread of V, past the 1e-2 bound in the
+    // tail of N(0,1) data.  Each weight's residual joins the product: a
+    // 16x16x32 product over [weights, residuals] x [V rows, the same V rows]
+    // (contraction slots 4..7 of a lane repeat its tokens g + 4e), so P.V
+    // and the normaliser see the weights to ~2^-16 in one instruction.
     const u32x2 pl = residual_pack<DT>(p, pa);
     st.lsum = packed_sum<DT>(pl, st.lsum);
+    const u32x4 pp{pa[0], pa[1], pl[0], pl[1]};
 #pragma unroll
-    for (int jj = 0; jj < S::EPL; ++jj) st.o[jj] = mfma_pv<DT>(pl, vb[jj], st.o[jj]);
+    for (int jj = 0; jj < S::EPL; ++jj)
+      st.o[jj] = mfma_qk<DT>(pp, u32x4{vb[jj][0], vb[jj][1], vb[jj][0], vb[jj][1]}, st.o[jj]);
+  } else {
+#pragma unroll
+    for (int jj = 0; jj < S::EPL; ++jj) st.o[jj] = mfma_pv<DT>(pa, vb[jj], st.o[jj]);
   }
 }
 
