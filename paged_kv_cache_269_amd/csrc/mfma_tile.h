@@ -6,8 +6,10 @@
 // O += P (16 rows x 16 tokens) . V_blk (16 x D), both on MFMA:
 //   S:  v_mfma_f32_16x16x32_{bf16,f16}, D/32 of them (rows = tokens,
 //       columns = query rows, contraction over head_dim);
-//   PV: v_mfma_f32_16x16x16_{bf16,f16}, D/16 of them (rows = query rows,
-//       columns = output dims, contraction over the block's 16 tokens).
+//   PV: v_mfma_f32_16x16x16_f16, D/16 of them (rows = query rows,
+//       columns = output dims, contraction over the block's 16 tokens); for
+//       bf16 v_mfma_f32_16x16x32_bf16 over the weights and their residuals
+//       against the same V rows twice (fold_tile).
 //
 // Lane layouts (wave64, lane l, n = l % 16, g = l / 16):
 //   MFMA 16x16xK operand A: row n, contraction slice g;  B: column n, slice g;
