@@ -2,12 +2,12 @@
 
 * 65535 sequences (the largest num_seqs: sequences are a grid dimension),
   past the 256 sequences up to which decode items take the longest-first
-  order: the vector path (MHA), the matrix-core path (8 query heads per KV
-  head) and the one-call step, every output row.
+  order: the vector path (MHA) and the matrix-core path (8 query heads per KV
+  head, bf16 and f16) and the one-call step, every output row.
 * One context cut into 2500 partitions (16-token partitions of 40000
   tokens): the workgroup-per-row reduce sweeps its weights in chunks of 512.
 * 65535 query tokens in one multi-query call (the largest num_query_tokens),
-  128 rows per KV head (wide items), every row.
+  120 rows per KV head (wide items), bf16 and f16, every row.
 * The reduce alone with 1100 partitions a row.
 """
 import sys
@@ -40,7 +40,7 @@ def pool_for(lens):
     return int(1.2 * sum((L + 15) // 16 for L in lens)) + 4
 
 
-@pytest.mark.parametrize("dtype,G", [("f16", 1), ("bf16", 8)])
+@pytest.mark.parametrize("dtype,G", [("f16", 1), ("bf16", 8), ("f16", 8)])
 def test_decode_max_sequences(cuda, dtype, G):
     import paged_kv_cache_269_amd as pa
     announce("decode, sequences", MAX_GRID, dtype, "G", G)
@@ -79,12 +79,13 @@ def test_decode_thousands_of_partitions(cuda):
     check_close(got, oracle_all(w), w.dtype, "16-token partitions of 40000 tokens")
 
 
-def test_multi_query_max_tokens(cuda):
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_multi_query_max_tokens(cuda, dtype):
     import paged_kv_cache_269_amd as pa
     nseq, n = MAX_GRID // 15, 15          # 4369 sequences x 15 tokens = 65535
-    announce("multi-query, query tokens", nseq * n)
+    announce("multi-query, query tokens", nseq * n, dtype)
     lens = (np.random.default_rng(4).integers(n, 60, nseq)).tolist()
-    w = W.generate("tiny", dtype="bf16", num_seqs=nseq, num_kv_heads=2, num_q_heads=16,
+    w = W.generate("tiny", dtype=dtype, num_seqs=nseq, num_kv_heads=2, num_q_heads=16,
                    head_dim=64, lens=lens, pool_blocks=pool_for(lens), seed=33)
     run = Run(w, cuda)
     run.reshape()
@@ -92,17 +93,18 @@ def test_multi_query_max_tokens(cuda):
     spans = W.generate_query_spans(w, n, seed=34)
     assert spans.q.shape[0] == MAX_GRID
     d = run.dev
-    q = torch.from_numpy(spans.q).view(torch.bfloat16).to(cuda)
+    q = torch.from_numpy(spans.q)
+    q = (q.view(torch.bfloat16) if dtype == "bf16" else q).to(cuda)
     qs = torch.from_numpy(spans.query_start).to(cuda)
     out = torch.full_like(q, float("nan"))
     pa.paged_attention_multi_query(out, q, d["k_cache"], d["v_cache"], d["block_tables"],
                                    d["context_lens"], qs, w.scale, w.max_context_len,
                                    spans.max_query_len)
     torch.cuda.synchronize()
-    got = to_f64(tensor_to_np(out, "bf16"), "bf16")
+    got = to_f64(tensor_to_np(out, dtype), dtype)
     ref = oracle.multi_query(spans.q, w.k_cache, w.v_cache, w.block_tables, w.context_lens,
                              spans.query_start, w.scale, w.dtype)
-    check_close(got, ref, "bf16", f"multi-query {MAX_GRID} tokens")
+    check_close(got, ref, dtype, f"multi-query {MAX_GRID} tokens {dtype}")
 
 
 def test_reduce_over_a_thousand_partitions(cuda):
