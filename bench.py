@@ -714,8 +714,9 @@ def main(argv=None) -> int:
     ms_per_step = wall * 1e3 / K
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     # Roofline of the step's launches over the timed region: one call of
-    # pa_reshape_and_decode (the KV write inside the decode kernel), or the
-    # KV-write kernel and the decode call.
+    # pa_reshape_and_decode (the KV write inside the decode kernel) or of
+    # pa_reshape_and_decode_cascade (the KV write inside the shared-prefix
+    # kernel), or the KV-write kernel and the decode call.
     dec_avg = region_ms / K
     launch_bytes = step_bytes
     achieved = launch_bytes / (dec_avg * 1e-3) / 1e9
@@ -753,8 +754,8 @@ def main(argv=None) -> int:
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic,
-                     "kernel": ("pa_reshape_and_decode_cascade (KV-write kernel, "
-                                "shared-prefix kernel, decode kernel)" if cascade and fused else
+                     "kernel": ("pa_reshape_and_decode_cascade (shared-prefix kernel with "
+                                "the KV write, decode kernel)" if cascade and fused else
                                 "pa_paged_attention_decode_cascade (KV-write kernel, "
                                 "shared-prefix kernel, decode kernel)" if cascade and
                                 not args.decode_only else

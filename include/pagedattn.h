@@ -255,12 +255,19 @@ int pa_paged_attention_decode_cascade(void* out, const void* q, const void* k_ca
 /*
  * The one-call step of the cascade entry point: each sequence's new token
  * (key, value [num_seqs, num_kv_heads, head_dim], slot_mapping [num_seqs])
- * written into the caches, then pa_paged_attention_decode_cascade -- the
- * same two steps enqueued by one call (the KV-write kernel runs first: after
- * the shared-prefix pass the decode items are short, and writing inside them
- * measured slower), so the result is the two calls' for any input.  Other
- * arguments, workspace and errors as for pa_paged_attention_decode_cascade;
- * key, value and slot_mapping must not be NULL when num_seqs > 0.
+ * written into the caches, then pa_paged_attention_decode_cascade.  The
+ * shared-prefix kernel stores the new rows (each of its workgroups those of
+ * its run of sequences, while it measures the shared part), so the decode
+ * kernel after it reads them from the caches; where that kernel does not run
+ * (fp32, more than 8 query heads per KV head, fewer than two sequences,
+ * block sizes other than 16) the KV-write kernel runs first.  Precondition as
+ * for pa_reshape_and_decode: no context reads, in this call, a slot written
+ * in this call other than its own last position (the shared-prefix kernel
+ * reads shared blocks while the rows are stored).  Under it the result is
+ * the two calls'; otherwise it is undefined (pa_validate_step_host checks
+ * it).  Other arguments, workspace and errors as for
+ * pa_paged_attention_decode_cascade; key, value and slot_mapping must not be
+ * NULL when num_seqs > 0.
  */
 int pa_reshape_and_decode_cascade(void* out, const void* q, const void* key, const void* value,
                                   void* k_cache, void* v_cache, const int64_t* slot_mapping,

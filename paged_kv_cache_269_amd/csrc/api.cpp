@@ -162,12 +162,19 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   // Grouped heads share every K/V tile: a matrix-core product pays off from
   // two heads up.  Single heads and fp32 stay on the vector ALU.
   const bool use_mfma = dtype != PA_F32 && group >= PA_MFMA_MIN_GROUP;
+  const bool prefix_pass = cascade && dtype != PA_F32 && group <= kCascadeMaxGroup &&
+                           num_seqs >= 2 && block_size == kBlock;
+  pa::KvWrite kw{};
   if (new_slots != nullptr) {
-    // New tokens' K/V: written by the decode kernel itself, except on the
-    // streaming kernel and in the cascade form, which are preceded by the
-    // KV-write kernel (the cascade's short items after the shared-prefix
-    // pass measured 1.3% slower doing the write themselves).
-    if ((use_mfma && pa::decode_mfma_streams(a)) || cascade) {
+    // New tokens' K/V: written by the decode kernel itself; in the cascade
+    // form by the shared-prefix kernel (the decode's short items after the
+    // shared-prefix pass measured 1.3% slower doing the write themselves);
+    // before the streaming kernel, and in a cascade without the
+    // shared-prefix pass, by the KV-write kernel.
+    if (prefix_pass) {
+      kw = pa::KvWrite{new_k, new_v, const_cast<void*>(k_cache), const_cast<void*>(v_cache),
+                       new_slots, num_blocks * block_size};
+    } else if ((use_mfma && pa::decode_mfma_streams(a)) || cascade) {
       if (pa::launch_reshape_and_cache(new_k, new_v, const_cast<void*>(k_cache),
                                        const_cast<void*>(v_cache), new_slots, num_seqs,
                                        num_kv_heads, head_dim, elem_bytes(dtype), block_size,
@@ -179,8 +186,7 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
       a.new_slots = new_slots;
     }
   }
-  if (cascade && dtype != PA_F32 && group <= kCascadeMaxGroup && num_seqs >= 2 &&
-      block_size == kBlock) {
+  if (prefix_pass) {
     // Shared-prefix pass first; the decode kernel then covers each
     // sequence's remaining blocks and merges the two parts.
     char* c = static_cast<char*>(workspace);
@@ -191,7 +197,7 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
     a.prefix_m = po.m;
     a.prefix_l = po.l;
     a.prefix_o = po.o;
-    if (pa::launch_prefix(a, po, dtype, head_dim, st) != hipSuccess) return PA_ERR_LAUNCH;
+    if (pa::launch_prefix(a, po, kw, dtype, head_dim, st) != hipSuccess) return PA_ERR_LAUNCH;
   }
   hipError_t e = use_mfma ? pa::launch_decode_mfma(a, dtype, head_dim, st)
                           : pa::launch_decode_valu(a, dtype, head_dim, st);

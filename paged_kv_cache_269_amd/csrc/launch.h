@@ -56,6 +56,18 @@ struct PrefixOut {
   float* o;
 };
 
+// The step's KV write when the shared-prefix kernel carries it: sequence s's
+// new K/V rows ([B, Hkv, D]) go to slot slots[s] of the pools (skipped when
+// the slot is negative or at or past num_slots).  slots == nullptr: no write.
+struct KvWrite {
+  const void* key;
+  const void* value;
+  void* k_cache;
+  void* v_cache;
+  const int64_t* slots;
+  int64_t num_slots;
+};
+
 // Multi-token queries (query tokens t of sequence s: query_start[s] <=
 // t < query_start[s + 1]).  `d.q` and `d.out` are [T, Hq, D]; the partials
 // are laid out as in decode with one row per (query token, query head).
@@ -116,9 +128,10 @@ bool decode_mfma_streams(const DecodeArgs& a);
 
 // Shared-prefix pass: for runs of consecutive sequences whose block tables
 // start with the same full blocks, the attention over those blocks, once per
-// run (f16/bf16, at most 8 query heads per KV head).
-hipError_t launch_prefix(const DecodeArgs& a, const PrefixOut& o, int dtype, int head_dim,
-                         hipStream_t stream);
+// run (f16/bf16, at most 8 query heads per KV head); with w.slots set it also
+// does the step's KV write (block size 16).
+hipError_t launch_prefix(const DecodeArgs& a, const PrefixOut& o, const KvWrite& w, int dtype,
+                         int head_dim, hipStream_t stream);
 
 // Matrix-core multi-query attention: one workgroup per (kv head x 16-row
 // unit, sequence, partition) item (f16/bf16).

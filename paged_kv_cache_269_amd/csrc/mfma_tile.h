@@ -287,6 +287,43 @@ __device__ __forceinline__ void fold_tile(MfmaState<D>& st, const u32x4 (&qb)[D 
   float mb = max_nn(max_nn(sc[0], sc[1]), max_nn(sc[2], sc[3]));
   mb = xor16_combine(mb, MaxNnOp{});
   mb = xor32_combine(mb, MaxNnOp{});
+  // The weights and the P.V products are written out in both arms of the
+  // rescale branch: each arm's products then update the accumulators in
+  // place.  With one copy after the branch the compiler keeps the rescaled
+  // accumulators apart and copies every accumulator register on the path
+  // without a rescale (the common one).
+  auto weights_and_products = [&]() __attribute__((always_inline)) {
+    float p[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) p[e] = fast_exp2(sc[e] - st.m);
+    if constexpr (MASKED) {
+      if (st.m == -INFINITY) {  // no valid token of this head so far
+#pragma unroll
+        for (int e = 0; e < 4; ++e) p[e] = 0.f;
+      }
+    }
+    const u32x2 pa{pack2<DT>(p[0], p[1]), pack2<DT>(p[2], p[3])};
+    // The normaliser sums the weights as rounded for P.V, so numerator and
+    // denominator weigh every token alike.
+    st.lsum = packed_sum<DT>(pa, st.lsum);
+    if constexpr (DT == kBF16) {
+      // bf16 weights carry 8 significant bits: one weight's rounding moves the
+      // output by up to 2^-8 of the spread of V, past the 1e-2 bound in the
+      // tail of N(0,1) data.  Each weight's residual joins the product: a
+      // 16x16x32 product over [weights, residuals] x [V rows, the same V rows]
+      // (contraction slots 4..7 of a lane repeat its tokens g + 4e), so P.V
+      // and the normaliser see the weights to ~2^-16 in one instruction.
+      const u32x2 pl = residual_pack<DT>(p, pa);
+      st.lsum = packed_sum<DT>(pl, st.lsum);
+      const u32x4 pp{pa[0], pa[1], pl[0], pl[1]};
+#pragma unroll
+      for (int jj = 0; jj < S::EPL; ++jj)
+        st.o[jj] = mfma_qk<DT>(pp, u32x4{vb[jj][0], vb[jj][1], vb[jj][0], vb[jj][1]}, st.o[jj]);
+    } else {
+#pragma unroll
+      for (int jj = 0; jj < S::EPL; ++jj) st.o[jj] = mfma_pv<DT>(pa, vb[jj], st.o[jj]);
+    }
+  };
   // The running max moves once a score passes it by more than kRescaleSlack,
   // so every weight stays below 2^kRescaleSlack.  The test is wave-uniform:
   // any row's rise rescales all.
@@ -304,36 +341,9 @@ __device__ __forceinline__ void fold_tile(MfmaState<D>& st, const u32x4 (&qb)[D 
     for (int jj = 0; jj < S::EPL; ++jj)
 #pragma unroll
       for (int e = 0; e < 4; ++e) st.o[jj][e] *= arow[e];
-  }
-  float p[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) p[e] = fast_exp2(sc[e] - st.m);
-  if constexpr (MASKED) {
-    if (st.m == -INFINITY) {  // no valid token of this head so far
-#pragma unroll
-      for (int e = 0; e < 4; ++e) p[e] = 0.f;
-    }
-  }
-  const u32x2 pa{pack2<DT>(p[0], p[1]), pack2<DT>(p[2], p[3])};
-  // The normaliser sums the weights as rounded for P.V, so numerator and
-  // denominator weigh every token alike.
-  st.lsum = packed_sum<DT>(pa, st.lsum);
-  if constexpr (DT == kBF16) {
-    // bf16 weights carry 8 significant bits: one weight's rounding moves the
-    // output by up to 2^-8 of the spread of V, past the 1e-2 bound in the
-    // tail of N(0,1) data.  Each weight's residual joins the product: a
-    // 16x16x32 product over [weights, residuals] x [V rows, the same V rows]
-    // (contraction slots 4..7 of a lane repeat its tokens g + 4e), so P.V
-    // and the normaliser see the weights to ~2^-16 in one instruction.
-    const u32x2 pl = residual_pack<DT>(p, pa);
-    st.lsum = packed_sum<DT>(pl, st.lsum);
-    const u32x4 pp{pa[0], pa[1], pl[0], pl[1]};
-#pragma unroll
-    for (int jj = 0; jj < S::EPL; ++jj)
-      st.o[jj] = mfma_qk<DT>(pp, u32x4{vb[jj][0], vb[jj][1], vb[jj][0], vb[jj][1]}, st.o[jj]);
+    weights_and_products();
   } else {
-#pragma unroll
-    for (int jj = 0; jj < S::EPL; ++jj) st.o[jj] = mfma_pv<DT>(pa, vb[jj], st.o[jj]);
+    weights_and_products();
   }
 }
 

@@ -94,7 +94,7 @@ __device__ __forceinline__ int group_prefix_blocks(const DecodeArgs& a, int s0, 
 }
 
 template <int DT, int D, int NW, int DEPTH>
-__global__ __launch_bounds__(NW * 64) void prefix_kernel(DecodeArgs a, PrefixOut out) {
+__global__ __launch_bounds__(NW * 64) void prefix_kernel(DecodeArgs a, PrefixOut out, KvWrite kw) {
   using S = MfmaShape<DT, D>;
   using VT = typename S::VT;
   __shared__ MfmaLds<D, NW> sm;
@@ -118,7 +118,40 @@ __global__ __launch_bounds__(NW * 64) void prefix_kernel(DecodeArgs a, PrefixOut
     for (int jj = 0; jj < S::NJ; ++jj)
       qb[jj] = ln.n < nrows ? q[qrow * S::CPR + 4 * jj + ln.g] : u32x4{0u, 0u, 0u, 0u};
   }
+  // The step's KV write for this run's sequences and KV head kvh: the new K
+  // and V rows to their slots (slot = block * 16 + offset, "vLLM 2026
+  // 推理引擎全解" §2.2), one 16-byte chunk per work-item and row half.  Its
+  // loads are issued with the table reads of the measurement below, whose
+  // wait covers them.
+  constexpr int WCH = kMaxRunSeqs * 2 * S::CPR;  // chunks of a full run (K and V)
+  constexpr int WPT = (WCH + NW * 64 - 1) / (NW * 64);
+  u32x4 wv[WPT];
+  int64_t wdst[WPT];
+  bool wk[WPT], wok[WPT];
+  if (kw.slots != nullptr) {
+#pragma unroll
+    for (int j = 0; j < WPT; ++j) {
+      const int i = (int)threadIdx.x + j * NW * 64;
+      const int tok = i / (2 * S::CPR), c = i % S::CPR;
+      wk[j] = (i / S::CPR) % 2 == 0;
+      wok[j] = tok < ns;
+      if (wok[j]) {
+        const int s = s0 + tok;
+        const int64_t src = ((int64_t)s * a.num_kv_heads + kvh) * S::CPR + c;
+        wv[j] = (wk[j] ? static_cast<const u32x4*>(kw.key) : static_cast<const u32x4*>(kw.value))[src];
+        const int64_t slot = kw.slots[s];
+        wok[j] = slot >= 0 && slot < kw.num_slots;
+        wdst[j] = (((slot / kBlockSize) * a.num_kv_heads + kvh) * kBlockSize + slot % kBlockSize) *
+                      S::CPR + c;
+      }
+    }
+  }
   const int P = group_prefix_blocks(a, s0, ns);
+  if (kw.slots != nullptr) {
+#pragma unroll
+    for (int j = 0; j < WPT; ++j)
+      if (wok[j]) (wk[j] ? static_cast<u32x4*>(kw.k_cache) : static_cast<u32x4*>(kw.v_cache))[wdst[j]] = wv[j];
+  }
   if (kvh == 0 && (int)threadIdx.x < ns) out.prefix_blocks[s0 + threadIdx.x] = P;
   if (P == 0) return;
 
@@ -155,7 +188,10 @@ __global__ __launch_bounds__(NW * 64) void prefix_kernel(DecodeArgs a, PrefixOut
         const int id = next_id;
         next_id = id_at(kn + 1);
         issue(kn, id, dn);
-        consume_any<DT, D>(st, qb, kr[d], vr[d], lim[d], a.scale_log2, ln, kst);
+        // a tile is whole or empty (past the end, or a block outside the
+        // pool): an empty one adds nothing to any row
+        if (lim[d] == kBlockSize)
+          consume_tile<DT, D, false>(st, qb, kr[d], vr[d], kBlockSize, a.scale_log2, ln, kst);
       });
     }
   }
@@ -212,26 +248,27 @@ __global__ __launch_bounds__(NW * 64) void prefix_kernel(DecodeArgs a, PrefixOut
 #endif
 
 template <int DT, int D>
-hipError_t launch_typed(const DecodeArgs& a, const PrefixOut& o, hipStream_t stream) {
+hipError_t launch_typed(const DecodeArgs& a, const PrefixOut& o, const KvWrite& w,
+                        hipStream_t stream) {
   const int G = a.num_q_heads / a.num_kv_heads;
   const int rs = 16 / G;
   const dim3 grid(a.num_kv_heads, (a.num_seqs + rs - 1) / rs);
   hipLaunchKernelGGL((prefix_kernel<DT, D, PA_PREFIX_WAVES, PA_PREFIX_DEPTH>), grid,
-                     dim3(PA_PREFIX_WAVES * 64), 0, stream, a, o);
+                     dim3(PA_PREFIX_WAVES * 64), 0, stream, a, o, w);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_prefix(const DecodeArgs& a, const PrefixOut& o, int dtype, int head_dim,
-                         hipStream_t stream) {
+hipError_t launch_prefix(const DecodeArgs& a, const PrefixOut& o, const KvWrite& w, int dtype,
+                         int head_dim, hipStream_t stream) {
   const int G = a.num_q_heads / a.num_kv_heads;
   if (G > 8) return hipErrorInvalidValue;
   switch (dtype * 1000 + head_dim) {
-    case kF16 * 1000 + 64: return launch_typed<kF16, 64>(a, o, stream);
-    case kF16 * 1000 + 128: return launch_typed<kF16, 128>(a, o, stream);
-    case kBF16 * 1000 + 64: return launch_typed<kBF16, 64>(a, o, stream);
-    case kBF16 * 1000 + 128: return launch_typed<kBF16, 128>(a, o, stream);
+    case kF16 * 1000 + 64: return launch_typed<kF16, 64>(a, o, w, stream);
+    case kF16 * 1000 + 128: return launch_typed<kF16, 128>(a, o, w, stream);
+    case kBF16 * 1000 + 64: return launch_typed<kBF16, 64>(a, o, w, stream);
+    case kBF16 * 1000 + 128: return launch_typed<kBF16, 128>(a, o, w, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -27,7 +27,7 @@ hipError_t launch_decode_mfma(const DecodeArgs&, int, int, hipStream_t) {
   return hipErrorInvalidValue;
 }
 bool decode_mfma_streams(const DecodeArgs&) { return false; }
-hipError_t launch_prefix(const DecodeArgs&, const PrefixOut&, int, int, hipStream_t) {
+hipError_t launch_prefix(const DecodeArgs&, const PrefixOut&, const KvWrite&, int, int, hipStream_t) {
   return hipErrorInvalidValue;
 }
 hipError_t launch_multi_query(const MultiQueryArgs&, int, int, hipStream_t) {
