@@ -432,8 +432,9 @@ int pa_validate_slots_host(const int64_t* slot_mapping, int32_t num_tokens,
                            int64_t num_blocks, int32_t block_size);
 
 /*
- * Host-side check of one decode step for pa_reshape_and_decode (host
- * pointers; one new token per sequence, slot_mapping [num_seqs]): the tables
+ * Host-side check of one decode step for pa_reshape_and_decode and
+ * pa_reshape_and_decode_cascade (host pointers; one new token per sequence,
+ * slot_mapping [num_seqs]): the tables
  * and the slots pass pa_validate_tables_host and pa_validate_slots_host, and
  * no context reads a slot written in this step other than the writer's own
  * last position context_lens[s] - 1 -- the condition under which the one-call

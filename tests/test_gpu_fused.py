@@ -245,6 +245,71 @@ def test_fused_cascade(cuda, case):
     announce(stats)
 
 
+@pytest.mark.parametrize("heads,dtype", [((32, 32), "bf16"), ((32, 8), "f16"), ((64, 8), "bf16")])
+def test_fused_cascade_slot_kinds(cuda, heads, dtype):
+    """The cascade one-call step (the shared-prefix kernel stores the new
+    rows) with slots of every kind, on pools whose contexts already end with
+    a written row: a context's last position (rewritten), padding (-1), past
+    the pool, and a block no context reads.  Pool and output equal the
+    KV-write kernel followed by the cascade call, bit for bit, and the
+    oracle's write (padded and past-the-pool rows are written nowhere)."""
+    import paged_kv_cache_269_amd as pa
+    Hq, Hkv = heads
+    w = W.generate("shared_prefix", num_seqs=12, num_q_heads=Hq, num_kv_heads=Hkv, dtype=dtype,
+                   len_lo=1, len_hi=100, seed=41)
+    bs, B = w.block_size, w.num_seqs
+    used = set(int(b) for b in w.block_tables.ravel())
+    free = [b for b in range(w.num_blocks) if b not in used]
+    slots = w.slot_mapping.copy()
+    for s in range(B):
+        if s % 4 == 1:
+            slots[s] = -1
+        elif s % 4 == 2:
+            slots[s] = w.num_blocks * bs + s          # past the pool
+        elif s % 4 == 3:
+            slots[s] = free.pop() * bs + s % bs       # a block no context reads
+    ok = slots.copy()
+    ok[ok >= w.num_blocks * bs] = -1
+    assert pa.validate_step_host(ok, w.block_tables, w.context_lens, w.num_blocks, bs) == 0
+    gen = np.random.default_rng(42)
+    key2 = W._round_to_dtype(gen.standard_normal(w.key.shape).astype(np.float32), dtype)
+    value2 = W._round_to_dtype(gen.standard_normal(w.value.shape).astype(np.float32), dtype)
+    announce("fused cascade slot kinds", heads, dtype)
+
+    def dev16(x):
+        t = torch.from_numpy(np.ascontiguousarray(x))
+        return (t.view(torch.bfloat16) if dtype == "bf16" else t).to(cuda)
+
+    k2, v2, sl = dev16(key2), dev16(value2), torch.from_numpy(slots).to(cuda)
+    runs = []
+    for _ in range(2):
+        r = Run(w, cuda)
+        r.reshape()  # every context now ends with its written row
+        runs.append(r)
+    d = runs[0].dev
+    out = torch.empty_like(d["q"])
+    pa.reshape_and_decode_cascade(out, d["q"], k2, v2, d["k_cache"], d["v_cache"], sl,
+                                  d["block_tables"], d["context_lens"], w.scale, w.max_context_len)
+    d = runs[1].dev
+    base = torch.empty_like(d["q"])
+    pa.reshape_and_cache(k2, v2, d["k_cache"], d["v_cache"], sl)
+    pa.paged_attention_decode_cascade(base, d["q"], d["k_cache"], d["v_cache"], d["block_tables"],
+                                      d["context_lens"], w.scale, w.max_context_len)
+    torch.cuda.synchronize()
+    assert np.array_equal(tensor_to_np(out, dtype).view(np.uint16),
+                          tensor_to_np(base, dtype).view(np.uint16)), "differs from the two calls"
+    kc, vc = pool_bits(runs[0], w)
+    kc2, vc2 = pool_bits(runs[1], w)
+    assert np.array_equal(kc, kc2) and np.array_equal(vc, vc2), "pools differ"
+    # the oracle: the first write, then this step's (it rejects a slot past
+    # the pool, which the kernels skip)
+    w2 = after_write(w)
+    oracle.reshape_and_cache(key2, value2, w2.k_cache, w2.v_cache, ok, dtype)
+    assert np.array_equal(kc, w2.k_cache.view(np.uint16)) and np.array_equal(vc, w2.v_cache.view(np.uint16))
+    check_close(to_f64(tensor_to_np(out, dtype), dtype), oracle_all(w2), dtype,
+                f"cascade slot kinds {heads} {dtype}")
+
+
 def test_fused_random_steps(cuda):
     """Seeded random steps (types, D, G, block sizes, partitions, lengths;
     slots at each context's last position, padding, or free blocks): whenever
