@@ -6,8 +6,9 @@ part-way (a member maps a private copy of one page: same data, another
 physical block); a context that ends exactly where the shared pages end; a
 shared part below the 4-block minimum; an empty and a 20-token context in a
 run; head groupings the shared pass handles (G <= 8, runs of 16 / G
-sequences) and beyond it (G = 16, plain decode); float32 (plain decode).
-Tolerances as for the plain decode.
+sequences) and beyond it (G = 16, plain decode); float32 (plain decode);
+8- and 32-token pools (plain decode; the one-call step's KV-write kernel
+first).  Tolerances as for the plain decode.
 """
 import sys
 
@@ -119,3 +120,36 @@ def test_cascade_workspace_reuse(cuda):
         run.oracle_reshape()
         got = to_f64(tensor_to_np(run_cascade(run, ws), "bf16"), "bf16")
         check_close(got, full_oracle(w), "bf16", f"workspace reuse B={w.num_seqs}")
+
+
+@pytest.mark.parametrize("bs", [8, 32])
+@pytest.mark.parametrize("G", [1, 4])
+def test_cascade_other_block_sizes(cuda, bs, G):
+    """8- and 32-token pools: the cascade entry points decode without the
+    shared-prefix pass (it works on 16-token blocks), and the one-call step
+    runs the KV-write kernel first.  The one call equals the KV-write kernel
+    plus the cascade call bit for bit (output and pool); both meet the
+    oracle."""
+    kw = dict(dtype="bf16", head_dim=128, num_kv_heads=2, num_q_heads=2 * G, num_seqs=12,
+              len_lo=1, len_hi=90, shared_prefix_blocks=128 // bs, block_size=bs, seed=23)
+    announce("cascade block size", bs, "G", G)
+    w1 = W.generate("shared_prefix", **kw)
+    run1 = Run(w1, cuda)  # the new tokens' slots hold NaN until written
+    d = run1.dev
+    one = torch.empty_like(d["q"])
+    run1.pa.reshape_and_decode_cascade(one, d["q"], d["key"], d["value"], d["k_cache"],
+                                       d["v_cache"], d["slot_mapping"], d["block_tables"],
+                                       d["context_lens"], w1.scale, w1.max_context_len)
+    torch.cuda.synchronize()
+    w2 = W.generate("shared_prefix", **kw)
+    run2 = Run(w2, cuda)
+    run2.reshape()
+    run2.oracle_reshape()
+    two = run_cascade(run2)
+    assert np.array_equal(tensor_to_np(one, "bf16").view(np.uint16),
+                          tensor_to_np(two, "bf16").view(np.uint16)), "one call != two calls"
+    for a, b in (("k_cache", "k_cache"), ("v_cache", "v_cache")):
+        assert np.array_equal(tensor_to_np(run1.dev[a], "bf16").view(np.uint16),
+                              tensor_to_np(run2.dev[b], "bf16").view(np.uint16)), a
+    check_close(to_f64(tensor_to_np(two, "bf16"), "bf16"), oracle_all(w2), "bf16",
+                f"cascade block size {bs} G{G}")
