@@ -6,8 +6,9 @@ that cross tile and block boundaries, whole prompts (n = L), an empty span,
 spans longer than the context (leading rows attend to nothing), chunks of
 33-128 tokens, head groups 1 to 16 (both item shapes, several items per KV
 head), block sizes 8/16/32, one pass and several partition sizes (the
-log-sum-exp reduce with per-token causal lengths), and the LLaMA-7B and GQA
-decode shapes with 4, 8 and 16 new tokens per sequence, every row.
+log-sum-exp reduce with per-token causal lengths), the LLaMA-7B and GQA
+decode shapes with 4, 8 and 16 new tokens per sequence, every row, and seeded
+random shapes (head groups up to 16, incl. 5 and 12).
 """
 import sys
 
@@ -167,3 +168,29 @@ def test_scale_sign_and_zero(cuda, scale):
         ref = oracle_mq(w, spans)
         got = to_f64(run_mq(run, spans, cuda, part), "bf16")
         check_close(got, ref, "bf16", f"scale {scale} G{G} partition {part}")
+
+
+def test_random_shapes(cuda):
+    """Seeded random cases: type, head_dim, KV heads, head groups (incl. 5
+    and 12, whose rows fill row tiles and wide items unevenly), block size,
+    partition size, 1-9 sequences of 0-700 tokens and spans of 0-40 tokens
+    (at most the context), every row against the oracle."""
+    rng = np.random.default_rng(2025)
+    for case in range(12):
+        dtype = ["f16", "bf16"][case % 2]
+        D = int(rng.choice([64, 128]))
+        Hkv = int(rng.integers(1, 4))
+        G = int(rng.choice([1, 2, 3, 4, 5, 8, 12, 16]))
+        bs = int(rng.choice([8, 16, 32]))
+        part = int(rng.choice([0, 16, 32, 64, 256, 1024]))
+        B = int(rng.integers(1, 10))
+        lens = [int(x) for x in rng.integers(0, 701, size=B)]
+        nqs = [int(rng.integers(0, min(L, 40) + 1)) for L in lens]
+        announce("random multi-query", case, dtype, D, Hkv, G, bs, part, lens, nqs)
+        w, run = prepared(cuda, dtype=dtype, head_dim=D, num_kv_heads=Hkv,
+                          num_q_heads=Hkv * G, lens=lens, seed=300 + case, block_size=bs)
+        spans = W.generate_query_spans(w, nqs, seed=400 + case)
+        if spans.q.shape[0] == 0:
+            continue
+        got = to_f64(run_mq(run, spans, cuda, part), dtype)
+        check_close(got, oracle_mq(w, spans), dtype, f"random case {case}")
