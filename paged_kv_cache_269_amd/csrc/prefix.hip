@@ -138,7 +138,8 @@ __global__ __launch_bounds__(NW * 64) void prefix_kernel(DecodeArgs a, PrefixOut
       if (wok[j]) {
         const int s = s0 + tok;
         const int64_t src = ((int64_t)s * a.num_kv_heads + kvh) * S::CPR + c;
-        wv[j] = (wk[j] ? static_cast<const u32x4*>(kw.key) : static_cast<const u32x4*>(kw.value))[src];
+        const u32x4* row = static_cast<const u32x4*>(wk[j] ? kw.key : kw.value);
+        wv[j] = row[src];
         const int64_t slot = kw.slots[s];
         wok[j] = slot >= 0 && slot < kw.num_slots;
         wdst[j] = (((slot / kBlockSize) * a.num_kv_heads + kvh) * kBlockSize + slot % kBlockSize) *
@@ -150,7 +151,7 @@ __global__ __launch_bounds__(NW * 64) void prefix_kernel(DecodeArgs a, PrefixOut
   if (kw.slots != nullptr) {
 #pragma unroll
     for (int j = 0; j < WPT; ++j)
-      if (wok[j]) (wk[j] ? static_cast<u32x4*>(kw.k_cache) : static_cast<u32x4*>(kw.v_cache))[wdst[j]] = wv[j];
+      if (wok[j]) static_cast<u32x4*>(wk[j] ? kw.k_cache : kw.v_cache)[wdst[j]] = wv[j];
   }
   if (kvh == 0 && (int)threadIdx.x < ns) out.prefix_blocks[s0 + threadIdx.x] = P;
   if (P == 0) return;
