@@ -690,8 +690,8 @@ def main(argv=None) -> int:
     args = parse_args(argv)
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU; "
-                                   f"--gpus {args.gpus} is not supported (no multi-GPU path "
-                                   "in this build)"}))
+                                   f"--gpus {args.gpus} is not supported (the library has no "
+                                   "multi-GPU path)"}))
         return 2
 
     import numpy as np
