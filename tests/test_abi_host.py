@@ -103,6 +103,35 @@ def test_fused_write_decode_argument_checks(hiplib):
     assert _fused(lib, B=0, key=None, slots=None) == OK
 
 
+def _fused_cascade(lib, **kw):
+    a = dict(out=FAKE, q=FAKE, key=FAKE, value=FAKE, k=FAKE, v=FAKE, slots=FAKE, bt=FAKE,
+             cl=FAKE, B=2, Hq=8, Hkv=2, D=128, bs=16, M=4, N=10, scale=0.1, dtype=1,
+             maxlen=64, ws=FAKE, wsb=1 << 20, stream=None)
+    a.update(kw)
+    return lib.pa_reshape_and_decode_cascade(a["out"], a["q"], a["key"], a["value"], a["k"],
+                                             a["v"], a["slots"], a["bt"], a["cl"], a["B"],
+                                             a["Hq"], a["Hkv"], a["D"], a["bs"], a["M"], a["N"],
+                                             a["scale"], a["dtype"], a["maxlen"], a["ws"],
+                                             a["wsb"], a["stream"])
+
+
+def test_fused_cascade_argument_checks(hiplib):
+    """pa_reshape_and_decode_cascade: the cascade checks, plus the new
+    tokens' rows and slots; all refused before any launch."""
+    lib = hiplib.load_library()
+    f = lib.pa_cascade_workspace_bytes
+    assert _fused_cascade(lib, key=None) == NULL
+    assert _fused_cascade(lib, value=None) == NULL
+    assert _fused_cascade(lib, slots=None) == NULL
+    assert _fused_cascade(lib, out=None) == NULL
+    assert _fused_cascade(lib, D=96) == UNSUP
+    assert _fused_cascade(lib, bs=24) == UNSUP
+    assert _fused_cascade(lib, Hq=6, Hkv=4) == SHAPE
+    assert _fused_cascade(lib, ws=None, wsb=0) == WS
+    assert _fused_cascade(lib, wsb=f(2, 8, 128) - 1) == WS
+    assert _fused_cascade(lib, B=0, key=None, slots=None, ws=None, wsb=0) == OK
+
+
 def test_workspace_bytes(hiplib):
     lib = hiplib.load_library()
     f = lib.pa_decode_workspace_bytes
