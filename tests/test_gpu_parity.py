@@ -97,7 +97,7 @@ EDGE_LENS = [1, 15, 16, 17, 511, 512, 513, 1024, 1025, 0, 2000]
     ("f32", 64, 1), ("f32", 128, 1), ("f32", 128, 4),
     ("f16", 64, 1), ("f16", 128, 1), ("f16", 64, 2), ("f16", 128, 8),
     ("bf16", 64, 1), ("bf16", 128, 1), ("bf16", 64, 8), ("bf16", 128, 8),
-    ("bf16", 128, 3), ("bf16", 128, 16), ("bf16", 128, 32),
+    ("bf16", 128, 3), ("bf16", 128, 16), ("bf16", 128, 32), ("f16", 128, 64), ("bf16", 64, 24),
 ])
 def test_edge_lengths_and_partitions(cuda, dtype, D, G):
     Hkv = 2
