@@ -71,7 +71,8 @@ def prepared(cuda, **kw):
 
 @pytest.mark.parametrize("dtype,D,Hkv,G,bs", [
     ("f16", 128, 2, 1, 16), ("bf16", 128, 2, 8, 16), ("bf16", 64, 2, 4, 8),
-    ("f16", 128, 2, 2, 32), ("bf16", 128, 1, 16, 16), ("f16", 64, 4, 3, 16)])
+    ("f16", 128, 2, 2, 32), ("bf16", 128, 1, 16, 16), ("f16", 64, 4, 3, 16),
+    ("bf16", 128, 1, 64, 16)])
 def test_ragged_spans(cuda, dtype, D, Hkv, G, bs):
     announce("multi-query ragged", dtype, D, Hkv, G, bs)
     w, run = prepared(cuda, dtype=dtype, head_dim=D, num_kv_heads=Hkv, num_q_heads=Hkv * G,
