@@ -17,11 +17,13 @@ constexpr float kLn2 = 0.6931471805599453f;
 // Online softmax of the matrix-core folds: how far (base 2) a tile's max may
 // pass the running max before the running max -- and with it the
 // accumulators' scale -- moves.  Weights then stay below 2^slack before
-// they are rounded to the 16-bit P operand; a slack of 1 rescales far less
-// often than 0 (every rise) with the same accuracy once the normaliser sums
-// the rounded weights (CPU emulation of the fold over seeded peaked rows).
+// they are rounded to the 16-bit P operand.  The normaliser sums the weights
+// as rounded, so the output is a weighted mean of V whose weights are off by
+// their own rounding only, relative to each weight whatever its size (f16:
+// 11 bits; bf16: weight and residual, ~16 bits): the slack sets how often
+// the accumulators are rescaled, not the accuracy.
 #ifndef PA_RESCALE_SLACK
-#define PA_RESCALE_SLACK 1
+#define PA_RESCALE_SLACK 8
 #endif
 constexpr float kRescaleSlack = PA_RESCALE_SLACK;
 
