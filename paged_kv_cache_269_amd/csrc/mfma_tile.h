@@ -100,7 +100,8 @@ __device__ __forceinline__ float packed_sum(const u32x2& w, float acc) {
   return add_pair<DT>(w[1], add_pair<DT>(w[0], acc));
 }
 
-// 16-bit element k of a row slice held as EPL elements.
+// A row slice of EPL 16-bit elements; pair() puts element k of two rows
+// side by side.
 template <int EPL>
 struct VSlice;
 template <>
@@ -108,8 +109,9 @@ struct VSlice<8> {
   using T = u32x4;
   template <bool SHARED>
   __device__ static __forceinline__ T load(Rsrc r, int off) { return buf_load16<SHARED>(r, off); }
-  __device__ static __forceinline__ uint32_t half(const T& v, int k) {
-    return (k & 1) ? (v[k >> 1] >> 16) : (v[k >> 1] & 0xffffu);
+  // element k of x in the low half, of y in the high half (one byte permute)
+  __device__ static __forceinline__ uint32_t pair(const T& x, const T& y, int k) {
+    return __builtin_amdgcn_perm(y[k >> 1], x[k >> 1], (k & 1) ? 0x07060302u : 0x05040100u);
   }
 };
 template <>
@@ -117,8 +119,8 @@ struct VSlice<4> {
   using T = u32x2;
   template <bool SHARED>
   __device__ static __forceinline__ T load(Rsrc r, int off) { return buf_load8<SHARED>(r, off); }
-  __device__ static __forceinline__ uint32_t half(const T& v, int k) {
-    return (k & 1) ? (v[k >> 1] >> 16) : (v[k >> 1] & 0xffffu);
+  __device__ static __forceinline__ uint32_t pair(const T& x, const T& y, int k) {
+    return __builtin_amdgcn_perm(y[k >> 1], x[k >> 1], (k & 1) ? 0x07060302u : 0x05040100u);
   }
 };
 
@@ -245,24 +247,29 @@ __device__ __forceinline__ void stage_k(u32x4* kst, u32x4 (&kr)[D / 32], const M
   get_k_stage<D>(kst, kr, ln);
 }
 
+// How many of a tile's 16 tokens count: all (kWhole); the first `limit`,
+// per token (kTokens); all or none, the same for the whole wave
+// (kWholeOrEmpty: an empty tile was loaded as zeros, so its V rows need no
+// clearing, and its weights are dropped as a whole).
+constexpr int kWhole = 0, kTokens = 1, kWholeOrEmpty = 2;
+
 // B operands of the tile's P.V products (product jj: this lane's tokens
 // g + 4e, element EPL*n + jj, packed in pairs), built once per tile; rows of
 // tokens past `limit` are zeroed first (whatever those slots hold must not
 // reach P.V, not even times a zero weight).
-template <int DT, int D, bool MASKED>
+template <int DT, int D, int MASKED>
 __device__ __forceinline__ void v_operands(typename MfmaShape<DT, D>::VT (&vr)[4], int limit,
                                            const MfmaLane& ln, u32x2 (&vb)[D / 16]) {
   using S = MfmaShape<DT, D>;
   using VT = typename S::VT;
-  if constexpr (MASKED) {
+  if constexpr (MASKED == kTokens) {
 #pragma unroll
     for (int e = 0; e < 4; ++e)
       if (ln.g + 4 * e >= limit) vr[e] = VT{};
   }
 #pragma unroll
   for (int jj = 0; jj < S::EPL; ++jj)
-    vb[jj] = u32x2{S::VS::half(vr[0], jj) | (S::VS::half(vr[1], jj) << 16),
-                   S::VS::half(vr[2], jj) | (S::VS::half(vr[3], jj) << 16)};
+    vb[jj] = u32x2{S::VS::pair(vr[0], vr[1], jj), S::VS::pair(vr[2], vr[3], jj)};
 }
 
 // Fold one tile into the state: K already in the S operand layout
@@ -270,7 +277,7 @@ __device__ __forceinline__ void v_operands(typename MfmaShape<DT, D>::VT (&vr)[4
 // one tile.  Scores of tokens at or past `row_limit` (per lane: its query
 // row n; the tile's token count, or less for causal rows of a multi-token
 // query) are dropped.
-template <int DT, int D, bool MASKED>
+template <int DT, int D, int MASKED>
 __device__ __forceinline__ void fold_tile(MfmaState<D>& st, const u32x4 (&qb)[D / 32],
                                           const u32x4 (&kr)[D / 32], const u32x2 (&vb)[D / 16],
                                           int row_limit, float scale_log2, const MfmaLane& ln) {
@@ -282,11 +289,12 @@ __device__ __forceinline__ void fold_tile(MfmaState<D>& st, const u32x4 (&qb)[D 
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     sc[e] = sacc[e] * scale_log2;
-    if constexpr (MASKED) sc[e] = ln.g + 4 * e < row_limit ? sc[e] : -INFINITY;
+    if constexpr (MASKED == kTokens) sc[e] = ln.g + 4 * e < row_limit ? sc[e] : -INFINITY;
   }
   float mb = max_nn(max_nn(sc[0], sc[1]), max_nn(sc[2], sc[3]));
   mb = xor16_combine(mb, MaxNnOp{});
   mb = xor32_combine(mb, MaxNnOp{});
+  if constexpr (MASKED == kWholeOrEmpty) mb = row_limit != 0 ? mb : -INFINITY;
   // The weights and the P.V products are written out in both arms of the
   // rescale branch: each arm's products then update the accumulators in
   // place.  With one copy after the branch the compiler keeps the rescaled
@@ -296,11 +304,15 @@ __device__ __forceinline__ void fold_tile(MfmaState<D>& st, const u32x4 (&qb)[D 
     float p[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) p[e] = fast_exp2(sc[e] - st.m);
-    if constexpr (MASKED) {
+    if constexpr (MASKED == kTokens) {
       if (st.m == -INFINITY) {  // no valid token of this head so far
 #pragma unroll
         for (int e = 0; e < 4; ++e) p[e] = 0.f;
       }
+    }
+    if constexpr (MASKED == kWholeOrEmpty) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) p[e] = row_limit != 0 ? p[e] : 0.f;
     }
     const u32x2 pa{pack2<DT>(p[0], p[1]), pack2<DT>(p[2], p[3])};
     // The normaliser sums the weights as rounded for P.V, so numerator and
@@ -349,7 +361,7 @@ __device__ __forceinline__ void fold_tile(MfmaState<D>& st, const u32x4 (&qb)[D 
 
 // Fold one tile (`limit` of its 16 tokens in the context) into the state:
 // stage K, build the V operands, fold.
-template <int DT, int D, bool MASKED>
+template <int DT, int D, int MASKED>
 __device__ __forceinline__ void consume_tile(MfmaState<D>& st, const u32x4 (&qb)[D / 32],
                                              u32x4 (&kr)[D / 32],
                                              typename MfmaShape<DT, D>::VT (&vr)[4], int limit,

@@ -170,7 +170,7 @@ __global__ __launch_bounds__(NW * 64) void prefix_kernel(DecodeArgs a, PrefixOut
   auto id_at = [&](int kk) -> int { return btc[w + min(kk, max(nk - 1, 0)) * NW]; };
   auto issue = [&](int kk, int bid, int slot) {
     const bool ok = kk < nk && (uint32_t)bid < (uint32_t)a.num_blocks_i32;
-    lim[slot] = ok ? kBlockSize : 0;
+    lim[slot] = __builtin_amdgcn_readfirstlane(ok ? kBlockSize : 0);
     load_tile<DT, D, true>(tile_desc<kBlockSize, S::TILE_BYTES>(a, TileIds<kBlockSize>{{bid}},
                                                                 w + kk * NW, kvh, ok),
                            ln, kr[slot], vr[slot]);
@@ -190,9 +190,9 @@ __global__ __launch_bounds__(NW * 64) void prefix_kernel(DecodeArgs a, PrefixOut
         next_id = id_at(kn + 1);
         issue(kn, id, dn);
         // a tile is whole or empty (past the end, or a block outside the
-        // pool): an empty one adds nothing to any row
-        if (lim[d] == kBlockSize)
-          consume_tile<DT, D, false>(st, qb, kr[d], vr[d], kBlockSize, a.scale_log2, ln, kst);
+        // pool): an empty one adds nothing to any row.  Folded either way
+        // (with its weights dropped), so the accumulators stay in place.
+        consume_tile<DT, D, kWholeOrEmpty>(st, qb, kr[d], vr[d], lim[d], a.scale_log2, ln, kst);
       });
     }
   }
