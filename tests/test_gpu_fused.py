@@ -314,7 +314,10 @@ def test_fused_random_steps(cuda):
     """Seeded random steps (types, D, G, block sizes, partitions, lengths;
     slots at each context's last position, padding, or free blocks): whenever
     pa_validate_step_host accepts a step, the one call equals the two calls
-    bit for bit (output and pool)."""
+    bit for bit (output and pool), and every row whose context the step
+    completes (its slot at the context's last position) equals the oracle's
+    after the oracle's KV write.  The other rows read a last position left as
+    NaN by the generator, in both paths alike."""
     import paged_kv_cache_269_amd as pa
     rng = np.random.default_rng(2024)
     for case in range(12):
@@ -329,6 +332,7 @@ def test_fused_random_steps(cuda):
         w = W.generate("long_context", dtype=dtype, head_dim=D, num_kv_heads=Hkv,
                        num_q_heads=Hkv * G, lens=lens, seed=100 + case, block_size=bs)
         slots = w.slot_mapping.copy()
+        last = w.slot_mapping.copy()
         # some sequences write nothing, some write into a block no context reads
         used = set(int(b) for s in range(B)
                    for b in w.block_tables[s, :(int(w.context_lens[s]) + bs - 1) // bs])
@@ -353,3 +357,8 @@ def test_fused_random_steps(cuda):
                               tensor_to_np(base, dtype).view(view)), f"case {case}: output"
         for x, y in zip(pool_bits(run, w), pool_bits(base_run, w)):
             assert np.array_equal(x, y), f"case {case}: pool"
+        oracle.reshape_and_cache(w.key, w.value, w.k_cache, w.v_cache, slots, dtype)
+        done = [s for s in range(B) if slots[s] == last[s] or w.context_lens[s] == 0]
+        if done:
+            check_close(to_f64(tensor_to_np(out, dtype), dtype)[done], oracle_all(w)[done], dtype,
+                        f"random step {case} against the oracle")
