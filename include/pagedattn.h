@@ -148,9 +148,9 @@ int pa_paged_attention_decode(void* out, const void* q, const void* k_cache,
  * The decode kernels then store each new row once and use it from registers
  * where a context ends with it, so no kernel waits for the write; when the
  * precondition does not hold the result is undefined (pa_validate_step_host
- * checks it on host copies of the step).  The streaming kernel
- * (16-token blocks, >= 8 partitions, <= 64 sequences, grouped heads) is
- * preceded by the KV-write kernel instead.
+ * checks it on host copies of the step).  Every decode kernel does this,
+ * the streaming one (16-token blocks, >= 8 partitions, <= 64 sequences,
+ * grouped heads) included.
  */
 int pa_reshape_and_decode(void* out, const void* q, const void* key, const void* value,
                           void* k_cache, void* v_cache, const int64_t* slot_mapping,

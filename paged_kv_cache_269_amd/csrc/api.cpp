@@ -168,13 +168,13 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
   if (new_slots != nullptr) {
     // New tokens' K/V: written by the decode kernel itself; in the cascade
     // form by the shared-prefix kernel (the decode's short items after the
-    // shared-prefix pass measured 1.3% slower doing the write themselves);
-    // before the streaming kernel, and in a cascade without the
-    // shared-prefix pass, by the KV-write kernel.
+    // shared-prefix pass measured 1.3% slower doing the write themselves),
+    // and in a cascade without the shared-prefix pass by the KV-write
+    // kernel.
     if (prefix_pass) {
       kw = pa::KvWrite{new_k, new_v, const_cast<void*>(k_cache), const_cast<void*>(v_cache),
                        new_slots, num_blocks * block_size};
-    } else if ((use_mfma && pa::decode_mfma_streams(a)) || cascade) {
+    } else if (cascade) {
       if (pa::launch_reshape_and_cache(new_k, new_v, const_cast<void*>(k_cache),
                                        const_cast<void*>(v_cache), new_slots, num_seqs,
                                        num_kv_heads, head_dim, elem_bytes(dtype), block_size,

@@ -8,7 +8,8 @@
 // G < 16 leaves rows idle (the matrix cores are far from the limit here, HBM
 // is).  Partial states of the NW waves of a workgroup are merged in LDS at
 // the end of the partition; one-wave items and the streaming kernel write
-// theirs from registers.
+// theirs from registers.  Every kernel here also does the one-call step's
+// KV write (items.h, new_token).
 #include <type_traits>
 
 #include "common.h"
@@ -440,6 +441,22 @@ __global__ __launch_bounds__(NW * 64, PA_STREAM_MIN_WAVES) void decode_mfma_stre
   }
   StreamCursor cc = lc;  // consume cursor
 
+  // Fused KV write (as in the items): each head tile's sequence's new row
+  // for the tile's KV head is loaded just before the tile's query (so the
+  // wait for q covers it); the tile holding the context's last position
+  // takes the row from registers where the slot is that position, and the
+  // item of the last partition of the KV head's first head chunk stores it.
+  constexpr int RB = D * 2;  // bytes of one K or V row
+  NewToken nt;
+  u32x4 nkc;
+  VT nvc;
+  auto new_row = [&]() {
+    nt = new_token<kBlockSize>(a, tables + cc.row, cc.s, cc.kvh, cc.len, true, RB);
+    nkc = buf_load16(new_row_rsrc(a, a.new_k, cc.s, cc.kvh, RB), (lane % S::CPR) * 16);
+    nvc = S::VS::template load<false>(new_row_rsrc(a, a.new_v, cc.s, cc.kvh, RB),
+                                      S::EPL * ln.n * 2);
+  };
+  new_row();
   HeadTile t = head_tile(a, cc.unit, cc.s);
   u32x4 qb[S::NJ];
   load_q<DT, D>(a, t, ln, qb);
@@ -476,13 +493,22 @@ __global__ __launch_bounds__(NW * 64, PA_STREAM_MIN_WAVES) void decode_mfma_stre
       issue(dn, id);
       next_id = id_of(lc);
       if (running) {
-        if (cc.new_tile) {  // a new head tile: its query
+        if (cc.new_tile) {  // a new head tile: its query (and new row)
+          new_row();
           t = head_tile(a, cc.unit, cc.s);
           load_q<DT, D>(a, t, ln, qb);
           // Wait for q here, on this rare path: left pending past the
           // branch, it would make every step wait for all loads in flight.
           wait_loaded(qb);
           cc.new_tile = false;
+        }
+        if (nt.sub && cc.j == nt.tile) {  // the context's last token is the new one
+#pragma unroll
+          for (int jj = 0; jj < S::NJ; ++jj)
+            if ((jj * 64 + lane) / S::CPR == nt.row) kr[d][jj] = nkc;
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (ln.g + 4 * e == nt.row) vr[d][e] = nvc;
         }
         consume_any<DT, D>(st, qb, kr[d], vr[d], lim[d], a.scale_log2, ln, kst);
         bool closed = false;
@@ -500,6 +526,10 @@ __global__ __launch_bounds__(NW * 64, PA_STREAM_MIN_WAVES) void decode_mfma_stre
             } else {
               write_wave_item<DT, D>(a, st, t, seg_part0, cc.nparts, ln);
               mark_empty(a, t, seg_part0 + 1, cc.part, ln);
+            }
+            if (nt.store && cc.unit % hchunks == 0 && cc.part == cc.nparts - 1) {
+              if (lane < S::CPR) store_row_part(a.k_cache, nt.off + lane * 16, nkc);
+              if (ln.g == 0) store_row_part(a.v_cache, nt.off + S::EPL * ln.n * 2, nvc);
             }
             st.reset();
             running = more;
@@ -601,7 +631,6 @@ hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
   const int64_t items = (int64_t)a.num_kv_heads * ((group + 15) / 16) * a.num_seqs *
                         a.max_partitions;
   if (decode_mfma_streams(a)) {
-    if (a.new_slots != nullptr) return hipErrorInvalidValue;  // the streaming kernel does no KV write
     return launch_stream_shape<DT, D, PA_MFMA_STREAM_WAVES, PA_MFMA_STREAM_DEPTH>(a, items, stream);
   }
   if (a.max_partitions >= kWaveItemParts)
