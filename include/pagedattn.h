@@ -260,7 +260,8 @@ int pa_paged_attention_decode_cascade(void* out, const void* q, const void* k_ca
  * its run of sequences, while it measures the shared part), so the decode
  * kernel after it reads them from the caches; where that kernel does not run
  * (fp32, more than 8 query heads per KV head, fewer than two sequences,
- * block sizes other than 16) the KV-write kernel runs first.  Precondition as
+ * block sizes other than 16) the decode kernels store them, as in
+ * pa_reshape_and_decode.  Precondition as
  * for pa_reshape_and_decode: no context reads, in this call, a slot written
  * in this call other than its own last position (the shared-prefix kernel
  * reads shared blocks while the rows are stored).  Under it the result is

@@ -166,20 +166,12 @@ int decode_impl(void* out, const void* q, const void* k_cache, const void* v_cac
                            num_seqs >= 2 && block_size == kBlock;
   pa::KvWrite kw{};
   if (new_slots != nullptr) {
-    // New tokens' K/V: written by the decode kernel itself; in the cascade
-    // form by the shared-prefix kernel (the decode's short items after the
-    // shared-prefix pass measured 1.3% slower doing the write themselves),
-    // and in a cascade without the shared-prefix pass by the KV-write
-    // kernel.
+    // New tokens' K/V: written by the decode kernel itself; where the
+    // shared-prefix pass runs, by the shared-prefix kernel (the decode's
+    // short items after it measured 1.3% slower doing the write themselves).
     if (prefix_pass) {
       kw = pa::KvWrite{new_k, new_v, const_cast<void*>(k_cache), const_cast<void*>(v_cache),
                        new_slots, num_blocks * block_size};
-    } else if (cascade) {
-      if (pa::launch_reshape_and_cache(new_k, new_v, const_cast<void*>(k_cache),
-                                       const_cast<void*>(v_cache), new_slots, num_seqs,
-                                       num_kv_heads, head_dim, elem_bytes(dtype), block_size,
-                                       num_blocks, st) != hipSuccess)
-        return PA_ERR_LAUNCH;
     } else {
       a.new_k = new_k;
       a.new_v = new_v;

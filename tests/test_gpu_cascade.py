@@ -7,8 +7,8 @@ physical block); a context that ends exactly where the shared pages end; a
 shared part below the 4-block minimum; an empty and a 20-token context in a
 run; head groupings the shared pass handles (G <= 8, runs of 16 / G
 sequences) and beyond it (G = 16, plain decode); float32 (plain decode);
-8- and 32-token pools (plain decode; the one-call step's KV-write kernel
-first).  Tolerances as for the plain decode.
+8- and 32-token pools (plain decode; in the one-call step the decode
+kernels store the new rows).  Tolerances as for the plain decode.
 """
 import sys
 
@@ -126,10 +126,10 @@ def test_cascade_workspace_reuse(cuda):
 @pytest.mark.parametrize("G", [1, 4])
 def test_cascade_other_block_sizes(cuda, bs, G):
     """8- and 32-token pools: the cascade entry points decode without the
-    shared-prefix pass (it works on 16-token blocks), and the one-call step
-    runs the KV-write kernel first.  The one call equals the KV-write kernel
-    plus the cascade call bit for bit (output and pool); both meet the
-    oracle."""
+    shared-prefix pass (it works on 16-token blocks), and in the one-call
+    step the decode kernels store the new rows.  The one call equals the
+    KV-write kernel plus the cascade call bit for bit (output and pool); both
+    meet the oracle."""
     kw = dict(dtype="bf16", head_dim=128, num_kv_heads=2, num_q_heads=2 * G, num_seqs=12,
               len_lo=1, len_hi=90, shared_prefix_blocks=128 // bs, block_size=bs, seed=23)
     announce("cascade block size", bs, "G", G)

@@ -219,6 +219,10 @@ def cascade_two_calls(w, cuda):
     ("shared_prefix", dict(num_seqs=10, num_q_heads=64, num_kv_heads=8, dtype="f16",
                            len_lo=1, len_hi=40)),                          # G = 8, short suffixes
     ("shared_prefix", {}),                                                  # full size
+    # no shared-prefix pass: the decode kernels store the new rows
+    ("shared_prefix", dict(num_seqs=9, dtype="f32", len_lo=1, len_hi=60)),   # fp32
+    ("shared_prefix", dict(num_seqs=6, num_q_heads=32, num_kv_heads=2)),    # G = 16
+    ("shared_prefix", dict(num_seqs=1, len_lo=1, len_hi=60)),               # one sequence
 ])
 def test_fused_cascade(cuda, case):
     """pa_reshape_and_decode_cascade on shared-prefix batches (new-token slots
