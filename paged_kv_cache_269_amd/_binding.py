@@ -97,6 +97,12 @@ def load_library() -> ctypes.CDLL:
     global _lib
     if _lib is not None:
         return _lib
+    # torch ships its own copy of the HIP runtime.  The library must run on
+    # that same copy, since it receives torch's device memory and streams:
+    # loaded first, the library would pull in the system runtime as well, and
+    # its launches on torch's streams would be refused.  With torch loaded
+    # first, the library binds to torch's runtime (same soname).
+    import torch  # noqa: F401
     if not os.path.exists(_LIB_PATH):
         raise RuntimeError(f"{_LIB_PATH} is missing: build it first "
                            "(python -m paged_kv_cache_269_amd.build)")

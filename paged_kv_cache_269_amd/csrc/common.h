@@ -26,6 +26,16 @@ constexpr float kLn2 = 0.6931471805599453f;
 #define PA_RESCALE_SLACK 8
 #endif
 constexpr float kRescaleSlack = PA_RESCALE_SLACK;
+// f16 weights (5 exponent bits) fall below the smallest subnormal, 2^-24,
+// 24 below the running max.  For f16 the running max is therefore kept
+// kF16MaxOffset below the largest score seen: the largest weight is 2^7 (and
+// with the slack at most 2^15, under the f16 limit of 65504), and a weight
+// only underflows 31 below it.  The state stays self-consistent (the sum is
+// taken against the same reference), so merges and exports are unchanged.
+// bf16 has the exponent range of f32 and keeps the plain running max.
+constexpr float kF16MaxOffset = 7.f;
+template <int DT>
+constexpr float kMaxOffset = DT == kF16 ? kF16MaxOffset : 0.f;
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));

@@ -79,6 +79,7 @@ __global__ __launch_bounds__(kCopyThreads) void swap_blocks_kernel(
 hipError_t launch_swap_blocks(const void* src, void* dst, const int64_t* pairs, int num_pairs,
                               int64_t block_bytes, int64_t src_blocks, int64_t dst_blocks,
                               hipStream_t stream) {
+  clear_stale_error();
   const int64_t chunks = block_bytes / 16;
   const int64_t per_block = (block_bytes + kCopyChunkBytes - 1) / kCopyChunkBytes;
   hipLaunchKernelGGL(swap_blocks_kernel, dim3((unsigned)per_block, (unsigned)num_pairs),
@@ -89,6 +90,7 @@ hipError_t launch_swap_blocks(const void* src, void* dst, const int64_t* pairs, 
 
 hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int num_pairs,
                               int64_t block_bytes, int64_t num_blocks, hipStream_t stream) {
+  clear_stale_error();
   const int64_t chunks = block_bytes / 16;
   const int64_t per_block = (block_bytes + kCopyChunkBytes - 1) / kCopyChunkBytes;
   hipLaunchKernelGGL(copy_blocks_kernel, dim3((unsigned)per_block, (unsigned)num_pairs),

@@ -651,6 +651,7 @@ bool decode_mfma_streams(const DecodeArgs& a) {
 }
 
 hipError_t launch_decode_mfma(const DecodeArgs& a, int dtype, int head_dim, hipStream_t stream) {
+  clear_stale_error();
   switch (dtype * 1000 + head_dim) {
     case kF16 * 1000 + 64: return launch_typed<kF16, 64>(a, stream);
     case kF16 * 1000 + 128: return launch_typed<kF16, 128>(a, stream);

@@ -388,6 +388,7 @@ hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_decode_valu(const DecodeArgs& a, int dtype, int head_dim, hipStream_t stream) {
+  clear_stale_error();
   switch (dtype * 1000 + head_dim) {
     case kF32 * 1000 + 64: return launch_typed<kF32, 64>(a, stream);
     case kF32 * 1000 + 128: return launch_typed<kF32, 128>(a, stream);

@@ -141,6 +141,13 @@ hipError_t launch_multi_query(const MultiQueryArgs& a, int dtype, int head_dim,
 hipError_t launch_reduce(const ReduceArgs& a, int dtype, int head_dim, int num_seqs,
                          hipStream_t stream);
 
+// hipGetLastError() reports the last error of any runtime call made on this
+// thread, not only of the launch it follows.  Every launch function below
+// clears one left behind by an earlier call (another library's, or a failed
+// device query) before it launches, so the status it returns is that of its
+// own launches.
+inline void clear_stale_error() { (void)hipGetLastError(); }
+
 // Host: compute units of the current device (cached per device; <= 0 on a
 // runtime error).
 inline int compute_units() {

@@ -337,10 +337,12 @@ __device__ __forceinline__ void fold_tile(MfmaState<D>& st, const u32x4 (&qb)[D 
     }
   };
   // The running max moves once a score passes it by more than kRescaleSlack,
-  // so every weight stays below 2^kRescaleSlack.  The test is wave-uniform:
-  // any row's rise rescales all.
-  if (__builtin_amdgcn_ballot_w64(mb > st.m + kRescaleSlack) != 0) {
-    const float mn = max_nn(st.m, mb);
+  // so every weight stays below 2^kRescaleSlack (for f16 the reference sits
+  // kF16MaxOffset below the largest score: weights below 2^(slack + offset)).
+  // The test is wave-uniform: any row's rise rescales all.
+  constexpr float OFF = kMaxOffset<DT>;
+  if (__builtin_amdgcn_ballot_w64(mb > st.m + (kRescaleSlack + OFF)) != 0) {
+    const float mn = max_nn(st.m, mb - OFF);
     const float alpha = mn == -INFINITY ? 1.f : fast_exp2(st.m - mn);
     st.lsum *= alpha;
     st.m = mn;

@@ -376,16 +376,16 @@ __device__ __forceinline__ void fold_group(MfmaState<D> (&st)[RT],
     // the largest raw score, scaled (scale_log2 >= 0 keeps it the largest)
     const float mr = xor32_combine(mb[r], MaxNnOp{});
     mb[r] = mr == -INFINITY ? -INFINITY : mr * scale_log2;
-    grow = grow || mb[r] > st[r].m + kRescaleSlack;
+    grow = grow || mb[r] > st[r].m + (kRescaleSlack + kMaxOffset<DT>);
   }
   // The running max moves once a score passes it by more than
-  // kRescaleSlack (weights stay below 2^kRescaleSlack).  Wave-uniform: a
-  // rescale to a larger max
-  // never changes the result, so all row tiles take it.
+  // kRescaleSlack (weights stay below 2^kRescaleSlack; for f16 the reference
+  // sits kF16MaxOffset below the largest score).  Wave-uniform: a rescale to
+  // a larger max never changes the result, so all row tiles take it.
   if (__builtin_amdgcn_ballot_w64(grow) != 0) {
 #pragma unroll
     for (int r = 0; r < RT; ++r) {
-      const float mn = max_nn(st[r].m, mb[r]);
+      const float mn = max_nn(st[r].m, mb[r] - kMaxOffset<DT>);
       const float alpha = mn == -INFINITY ? 1.f : fast_exp2(st[r].m - mn);
       st[r].lsum *= alpha;
       st[r].m = mn;
@@ -736,6 +736,7 @@ hipError_t launch_typed(const MultiQueryArgs& a, hipStream_t stream) {
 
 hipError_t launch_multi_query(const MultiQueryArgs& a, int dtype, int head_dim,
                               hipStream_t stream) {
+  clear_stale_error();
   switch (dtype * 1000 + head_dim) {
     case kF16 * 1000 + 64: return launch_typed<kF16, 64>(a, stream);
     case kF16 * 1000 + 128: return launch_typed<kF16, 128>(a, stream);

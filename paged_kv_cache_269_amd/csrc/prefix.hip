@@ -263,6 +263,7 @@ hipError_t launch_typed(const DecodeArgs& a, const PrefixOut& o, const KvWrite& 
 
 hipError_t launch_prefix(const DecodeArgs& a, const PrefixOut& o, const KvWrite& w, int dtype,
                          int head_dim, hipStream_t stream) {
+  clear_stale_error();
   const int G = a.num_q_heads / a.num_kv_heads;
   if (G > 8) return hipErrorInvalidValue;
   switch (dtype * 1000 + head_dim) {

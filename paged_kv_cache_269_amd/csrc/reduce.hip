@@ -200,6 +200,7 @@ hipError_t launch_typed(const ReduceArgs& a, int num_seqs, hipStream_t stream) {
 
 hipError_t launch_reduce(const ReduceArgs& a, int dtype, int head_dim, int num_seqs,
                          hipStream_t stream) {
+  clear_stale_error();
   switch (dtype * 1000 + head_dim) {
     case kF32 * 1000 + 64: return launch_typed<kF32, 64>(a, num_seqs, stream);
     case kF32 * 1000 + 128: return launch_typed<kF32, 128>(a, num_seqs, stream);

@@ -37,6 +37,7 @@ hipError_t launch_reshape_and_cache(const void* key, const void* value, void* k_
                                     void* v_cache, const int64_t* slot_mapping, int num_tokens,
                                     int num_kv_heads, int head_dim, int elem_bytes, int block_size,
                                     int64_t num_blocks, hipStream_t stream) {
+  clear_stale_error();
   const int chunks_per_row = head_dim * elem_bytes / 16;
   const int64_t total = (int64_t)num_tokens * num_kv_heads * chunks_per_row;
   const int threads = 256;

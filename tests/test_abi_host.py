@@ -413,3 +413,23 @@ def test_step_validator_matches_brute_force(hiplib):
         assert (got == OK) == want, (bt, cl, slots, bs, got)
         agree[want] += 1
     assert agree[True] > 20 and agree[False] > 20   # both outcomes exercised
+
+
+def test_library_binds_to_torchs_hip_runtime():
+    """Loaded before torch is imported, the library still ends up on torch's
+    copy of the HIP runtime (the one whose memory and streams it is given):
+    one libamdhip64 in the process, not the system's beside torch's.  Checked
+    in a fresh interpreter, which imports the package and loads the library
+    first."""
+    import ast
+    import subprocess
+    import sys
+    code = ("import paged_kv_cache_269_amd as pa; pa.load_library(); import torch; "
+            "print(sorted({l.split()[-1] for l in open('/proc/self/maps') "
+            "if 'libamdhip64' in l}))")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True,
+                       timeout=600, cwd=root)
+    assert r.returncode == 0, r.stderr[-2000:]
+    runtimes = ast.literal_eval(r.stdout.strip().splitlines()[-1])
+    assert len(runtimes) == 1, f"two HIP runtimes loaded: {runtimes}"
